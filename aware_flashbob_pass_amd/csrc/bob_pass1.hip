@@ -1,0 +1,301 @@
+// BoB pass 1: query-tile parallel. Produces gQ, gdO and the two row scalars.
+//
+// FlashBoB review page (Summary; Strengths on Prop. 4.1): the softmax double
+// backward has a hierarchical affine structure in which two row scalars,
+// alpha and E, enter every output affinely, so one sweep over the keys per
+// query tile can accumulate alpha-free sums and apply the scalars at the end.
+// Written out for row i (sums over keys j; G = tau (UQ K^T + Q UK^T),
+// H = dO UV^T, dP = dO V^T, P = exp(tau Q K^T - L)):
+//   alpha_i = sum_j P G,                   E_i = sum_j W_b - alpha_i D_i,
+//   W_a = P (dP - D),  W_b = P (G (dP - D) + H),
+//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i (P dP) K - E_i P K ],
+//   gdO_i = (P UV + (P G) V) - alpha_i O_i.
+// The six alpha-free contractions W_a UK, W_b K, (P dP) K, P K, P UV and
+// (P G) V accumulate into four float32 register tiles (A, B, C, X below); the
+// pages name six alpha-free accumulators without listing them, and this is our
+// reading of them.
+//
+// Each workgroup owns 128 queries (4 waves x 32) and a contiguous range of key
+// tiles (the whole key range, or one of `nsplit` parts of it). With splits,
+// each wave writes its raw accumulators and row partial sums as a record and
+// a combine kernel sums the records in split order and applies the epilogue.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fb {
+
+template <class TT, int D>
+struct P1 {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  static constexpr int MB = G::MB;
+  // record layout (floats): acc[4][MB][16][64 lanes], alpha_p[64], e0_p[64]
+  static constexpr int ACC_FLOATS = 4 * MB * 16 * 64;
+};
+
+// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave.
+template <class TT, int D>
+__device__ inline void pass1_epilogue(const f32x16 (&A)[Geo<TT, D>::MB], const f32x16 (&B)[Geo<TT, D>::MB],
+                                      const f32x16 (&C)[Geo<TT, D>::MB], const f32x16 (&X)[Geo<TT, D>::MB],
+                                      float alpha_p, float e0_p, int qi, int g, int bh,
+                                      const Pass1Args& a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  const int N = a.N;
+  const float alpha = alpha_p + xor32(alpha_p);
+  const float e0 = e0_p + xor32(e0_p);
+  if (qi >= N) return;
+  const size_t row = (size_t)bh * N + qi;
+  const float dq = a.D[row];
+  const float E = e0 - alpha * dq;
+  const T* O = reinterpret_cast<const T*>(a.O) + row * D;
+  T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
+  T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
+  const float tau = a.tau;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = mb * 32 + kappa(r4 * 4, g);
+      float o[4], q[4], x[4];
+      load4<TT>(O + dim, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r4 * 4 + e;
+        q[e] = tau * (A[mb][r] - alpha * B[mb][r] - E * C[mb][r]);
+        x[e] = X[mb][r] - alpha * o[e];
+      }
+      store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
+      store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
+    }
+  if (g == 0) {
+    a.alpha[row] = alpha;
+    a.E[row] = E;
+  }
+}
+
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBlock) void bob_pass1_kernel(Pass1Args a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  using V = typename TT::vec;
+  constexpr int MB = G::MB;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* k_r = reinterpret_cast<T*>(smem);
+  T* v_r = k_r + G::ROW_ELEMS;
+  T* uk_r = v_r + G::ROW_ELEMS;
+  T* uv_r = uk_r + G::ROW_ELEMS;
+  T* k_t = uv_r + G::ROW_ELEMS;
+  T* v_t = k_t + G::T_ELEMS;
+  T* uk_t = v_t + G::T_ELEMS;
+  T* uv_t = uk_t + G::T_ELEMS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  const size_t base = (size_t)bh * N * D;
+  const T* Q = reinterpret_cast<const T*>(a.Q) + base;
+  const T* K = reinterpret_cast<const T*>(a.K) + base;
+  const T* Vm = reinterpret_cast<const T*>(a.V) + base;
+  const T* dO = reinterpret_cast<const T*>(a.dO) + base;
+  const T* UQ = reinterpret_cast<const T*>(a.UQ) + base;
+  const T* UK = reinterpret_cast<const T*>(a.UK) + base;
+  const T* UV = reinterpret_cast<const T*>(a.UV) + base;
+  const int q0 = blockIdx.x * kBlockRows + wave * kTile;
+  const int qi = q0 + n;
+
+  V bq[G::DK], bdo[G::DK], buq[G::DK];
+  load_resident<TT, D>(Q, qi, N, g, bq);
+  load_resident<TT, D>(dO, qi, N, g, bdo);
+  load_resident<TT, D>(UQ, qi, N, g, buq);
+  const size_t rowv = (size_t)bh * N + (qi < N ? qi : 0);
+  const float lq = a.L[rowv] * kLog2e;
+  const float dq = a.D[rowv];
+  const float cs = a.tau * kLog2e;
+  const float tau = a.tau;
+
+  f32x16 accA[MB], accB[MB], accC[MB], accX[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = zero16();
+    accB[mb] = zero16();
+    accC[mb] = zero16();
+    accX[mb] = zero16();
+  }
+  float alpha_p = 0.f, e0_p = 0.f;
+
+  int nkt = (N + kTile - 1) / kTile;
+  if (CAUSAL) nkt = min(nkt, (int)(blockIdx.x + 1) * (kBlockRows / kTile));
+  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
+  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int k0 = kt * kTile;
+    __syncthreads();
+    stage_tile<TT, D>(K, k0, N, k_r, k_t, tid, kBlock);
+    stage_tile<TT, D>(Vm, k0, N, v_r, v_t, tid, kBlock);
+    stage_tile<TT, D>(UK, k0, N, uk_r, uk_t, tid, kBlock);
+    stage_tile<TT, D>(UV, k0, N, uv_r, uv_t, tid, kBlock);
+    __syncthreads();
+    if (CAUSAL && k0 > q0 + kTile - 1) continue;
+
+    // score tiles (keys x queries): S, G, dP, H
+    f32x16 s = zero16(), gg = zero16(), dp = zero16(), h = zero16();
+#pragma unroll
+    for (int t = 0; t < G::DK; ++t) {
+      const V ak = lds_row_op<TT, D>(k_r, n, t, g);
+      const V auk = lds_row_op<TT, D>(uk_r, n, t, g);
+      const V av = lds_row_op<TT, D>(v_r, n, t, g);
+      const V auv = lds_row_op<TT, D>(uv_r, n, t, g);
+      s = TT::mfma(ak, bq[t], s);
+      gg = TT::mfma(ak, buq[t], gg);
+      gg = TT::mfma(auk, bq[t], gg);
+      dp = TT::mfma(av, bdo[t], dp);
+      h = TT::mfma(auv, bdo[t], h);
+    }
+
+    // element-wise weights
+    V wa[G::NK], wb[G::NK], pd[G::NK], pp[G::NK], pg[G::NK];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + kappa(r, g);
+      const bool ok = key < N && (!CAUSAL || key <= qi);
+      const float p = ok ? fast_exp2(s[r] * cs - lq) : 0.f;
+      const float gv = gg[r] * tau;
+      const float dpv = dp[r];
+      const float t1 = dpv - dq;
+      const float vpg = p * gv;
+      const float vwb = p * (gv * t1 + h[r]);
+      alpha_p += vpg;
+      e0_p += vwb;
+      const int kk = r / TT::KPL, ss = r % TT::KPL;
+      vset<TT>(wa[kk], ss, p * t1);
+      vset<TT>(wb[kk], ss, vwb);
+      vset<TT>(pd[kk], ss, p * dpv);
+      vset<TT>(pp[kk], ss, p);
+      vset<TT>(pg[kk], ss, vpg);
+    }
+
+    // alpha-free accumulators (head dims x queries)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int dim = mb * 32 + n;
+#pragma unroll
+      for (int t = 0; t < G::NK; ++t) {
+        const V tk = lds_t_op<TT, D>(k_t, dim, t, g);
+        const V tuk = lds_t_op<TT, D>(uk_t, dim, t, g);
+        const V tv = lds_t_op<TT, D>(v_t, dim, t, g);
+        const V tuv = lds_t_op<TT, D>(uv_t, dim, t, g);
+        accA[mb] = TT::mfma(tuk, wa[t], accA[mb]);
+        accA[mb] = TT::mfma(tk, wb[t], accA[mb]);
+        accB[mb] = TT::mfma(tk, pd[t], accB[mb]);
+        accC[mb] = TT::mfma(tk, pp[t], accC[mb]);
+        accX[mb] = TT::mfma(tuv, pp[t], accX[mb]);
+        accX[mb] = TT::mfma(tv, pg[t], accX[mb]);
+      }
+    }
+  }
+
+  if (a.nsplit == 1) {
+    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
+    return;
+  }
+  const int qt_count = row_tiles(N);
+  const size_t rec = (((size_t)split * a.BH + bh) * qt_count + blockIdx.x) * 4 + wave;
+  float* R = a.part + rec * pass1_record_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      R[((0 * MB + mb) * 16 + r) * 64 + lane] = accA[mb][r];
+      R[((1 * MB + mb) * 16 + r) * 64 + lane] = accB[mb][r];
+      R[((2 * MB + mb) * 16 + r) * 64 + lane] = accC[mb][r];
+      R[((3 * MB + mb) * 16 + r) * 64 + lane] = accX[mb][r];
+    }
+  R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
+  R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;
+}
+
+// Sum the split records of each wave in split order, then apply the epilogue.
+template <class TT, int D>
+__global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) {
+  using G = Geo<TT, D>;
+  constexpr int MB = G::MB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = a.N, bh = blockIdx.y;
+  const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
+  const int qt_count = row_tiles(N);
+  f32x16 A[MB], B[MB], C[MB], X[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    A[mb] = zero16();
+    B[mb] = zero16();
+    C[mb] = zero16();
+    X[mb] = zero16();
+  }
+  float alpha_p = 0.f, e0_p = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const size_t rec = (((size_t)sp * a.BH + bh) * qt_count + blockIdx.x) * 4 + wave;
+    const float* R = a.part + rec * pass1_record_floats(D);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        A[mb][r] += R[((0 * MB + mb) * 16 + r) * 64 + lane];
+        B[mb][r] += R[((1 * MB + mb) * 16 + r) * 64 + lane];
+        C[mb][r] += R[((2 * MB + mb) * 16 + r) * 64 + lane];
+        X[mb][r] += R[((3 * MB + mb) * 16 + r) * 64 + lane];
+      }
+    alpha_p += R[P1<TT, D>::ACC_FLOATS + lane];
+    e0_p += R[P1<TT, D>::ACC_FLOATS + 64 + lane];
+  }
+  pass1_epilogue<TT, D>(A, B, C, X, alpha_p, e0_p, qi, g, bh, a);
+}
+
+template <class TT, int D>
+static size_t pass1_lds_bytes() {
+  using G = Geo<TT, D>;
+  return (size_t)4 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
+}
+
+template <class TT, int D, bool CAUSAL>
+static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
+  const size_t lds = pass1_lds_bytes<TT, D>();
+  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL>, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(row_tiles(a.N), a.BH, a.nsplit);
+  hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+template <class TT>
+static hipError_t launch_p1_tt(const Pass1Args& a, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? launch_p1_t<TT, 64, true>(a, s) : launch_p1_t<TT, 64, false>(a, s);
+  return causal ? launch_p1_t<TT, 128, true>(a, s) : launch_p1_t<TT, 128, false>(a, s);
+}
+
+hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return launch_p1_tt<BF16>(a, d, causal, s);
+    case DT::F16: return launch_p1_tt<F16>(a, d, causal, s);
+    default: return launch_p1_tt<F32>(a, d, causal, s);
+  }
+}
+
+template <class TT, int D>
+static hipError_t launch_c1_t(const Pass1Args& a, hipStream_t s) {
+  dim3 grid(row_tiles(a.N), a.BH);
+  hipLaunchKernelGGL((bob_pass1_combine_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return d == 64 ? launch_c1_t<BF16, 64>(a, s) : launch_c1_t<BF16, 128>(a, s);
+    case DT::F16: return d == 64 ? launch_c1_t<F16, 64>(a, s) : launch_c1_t<F16, 128>(a, s);
+    default: return d == 64 ? launch_c1_t<F32, 64>(a, s) : launch_c1_t<F32, 128>(a, s);
+  }
+}
+
+}  // namespace fb

@@ -1,0 +1,211 @@
+// Shared device helpers for the gfx950 attention BoB kernels.
+//
+// Tiling convention used by every kernel here. A wave owns 32 "resident" rows
+// (queries in the statistics kernel and pass 1, keys in pass 2) and walks the
+// other ("streamed") side in steps of 32 rows that the workgroup stages in LDS.
+// Each step forms 32x32 score tiles with v_mfma_f32_32x32x{16 bf16|16 f16|2 f32}
+// so that lane l owns resident row (l % 32) and, in its 16 accumulator slots
+// r = 0..15, the streamed rows kappa(r, l / 32) = 8*(r/4) + 4*(l/32) + r%4.
+// That is the matrix cores' own output layout with the resident side on the
+// N (column) axis: the score tile is S^T (streamed x resident).
+//
+// The accumulating contractions (sum over the streamed rows) then reuse each
+// lane's slots directly as the B operand: the contraction index k of slot r is
+// the streamed row kappa(r, g), and the A operand (streamed-tensor columns)
+// is read from a transposed LDS copy whose 32 columns are stored in the order
+// pos(k) with pos(kappa(r, g)) = 16*g + r, so that a lane's KPL operand
+// elements are contiguous. Outputs come out transposed as well (head dim on
+// the M axis, resident row on the N axis): lane l holds dims
+// kappa(r, l / 32) of resident row l % 32, so every per-row scalar (LSE, D,
+// alpha, E) is a per-lane value after one exchange between lanes l and l ^ 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fb {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 32;  // resident rows per wave == streamed rows per step
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element types and their matrix-core instruction -----------------------
+struct BF16 {
+  using elem = __bf16;
+  using vec = bf16x8;
+  static constexpr int KPL = 8;  // operand elements per lane per k-step
+  __device__ static inline f32x16 mfma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline elem cvt(float x) { return (elem)x; }
+  __device__ static inline float tof(elem x) { return (float)x; }
+};
+struct F16 {
+  using elem = _Float16;
+  using vec = f16x8;
+  static constexpr int KPL = 8;
+  __device__ static inline f32x16 mfma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline elem cvt(float x) { return (elem)x; }
+  __device__ static inline float tof(elem x) { return (float)x; }
+};
+struct F32 {
+  using elem = float;
+  using vec = float;
+  static constexpr int KPL = 1;
+  __device__ static inline f32x16 mfma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline elem cvt(float x) { return x; }
+  __device__ static inline float tof(elem x) { return x; }
+};
+
+template <class TT>
+__device__ inline void vset(typename TT::vec& v, int s, float x) {
+  if constexpr (TT::KPL == 1) {
+    v = x;
+  } else {
+    v[s] = TT::cvt(x);
+  }
+}
+
+__host__ __device__ constexpr int kappa(int r, int g) { return ((r >> 2) << 3) + (g << 2) + (r & 3); }
+__host__ __device__ constexpr int tpos(int k) { return (((k >> 2) & 1) << 4) + ((k >> 3) << 2) + (k & 3); }
+
+// ---- LDS tile geometry --------------------------------------------------------
+// Row-major copy: 32 rows x D, row stride RS elements. Transposed copy: D rows
+// (head dims) x 32 columns in tpos() order, row stride TS elements. The pads
+// keep 16-byte operand reads of consecutive lanes on distinct LDS banks.
+template <class TT, int D>
+struct Geo {
+  using T = typename TT::elem;
+  static constexpr int PAD = (sizeof(T) == 2) ? 8 : 1;
+  static constexpr int RS = D + PAD;
+  static constexpr int TS = kTile + PAD;
+  static constexpr int ROW_ELEMS = kTile * RS;
+  static constexpr int T_ELEMS = D * TS;
+  static constexpr int DK = D / (2 * TT::KPL);      // k-steps over the head dim
+  static constexpr int NK = kTile / (2 * TT::KPL);  // k-steps over 32 streamed rows
+  static constexpr int MB = D / 32;                 // 32-wide head-dim blocks
+};
+
+// Stage rows [r0, r0 + 32) of a [N][D] tensor into LDS (row-major copy `rowbuf`
+// and/or transposed copy `tbuf`, either may be null). Rows >= N read as zero.
+// All `nthreads` threads of the block take part; caller brackets with barriers.
+template <class TT, int D>
+__device__ inline void stage_tile(const typename TT::elem* __restrict__ src, int r0, int N,
+                                  typename TT::elem* rowbuf, typename TT::elem* tbuf, int tid,
+                                  int nthreads) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / CH;         // chunks per row
+  constexpr int NCH = kTile * CPR;
+  for (int c = tid; c < NCH; c += nthreads) {
+    const int row = c / CPR;
+    const int e0 = (c % CPR) * CH;
+    const int grow = r0 + row;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (grow < N) raw = *reinterpret_cast<const uint4*>(src + (size_t)grow * D + e0);
+    const T* v = reinterpret_cast<const T*>(&raw);
+    if (rowbuf) {
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4*>(rowbuf + row * G::RS + e0) = raw;
+      } else {
+#pragma unroll
+        for (int e = 0; e < CH; ++e) rowbuf[row * G::RS + e0 + e] = v[e];
+      }
+    }
+    if (tbuf) {
+      const int p = tpos(row);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) tbuf[(e0 + e) * G::TS + p] = v[e];
+    }
+  }
+}
+
+// A operand of a score tile: streamed row m = lane % 32, head dims of k-step t.
+template <class TT, int D>
+__device__ inline typename TT::vec lds_row_op(const typename TT::elem* rowbuf, int m, int t, int g) {
+  using G = Geo<TT, D>;
+  const typename TT::elem* p = rowbuf + m * G::RS + t * 2 * TT::KPL + g * TT::KPL;
+  return *reinterpret_cast<const typename TT::vec*>(p);
+}
+
+// A operand of an accumulating contraction: head dim `dim`, streamed rows of
+// k-step t (slots r = t*KPL .. t*KPL + KPL - 1 of lane group g).
+template <class TT, int D>
+__device__ inline typename TT::vec lds_t_op(const typename TT::elem* tbuf, int dim, int t, int g) {
+  using G = Geo<TT, D>;
+  const typename TT::elem* p = tbuf + dim * G::TS + g * 16 + t * TT::KPL;
+  return *reinterpret_cast<const typename TT::vec*>(p);
+}
+
+// B operand held in registers for the whole kernel: resident row `row`
+// (zero when row >= N), head dims of every k-step.
+template <class TT, int D>
+__device__ inline void load_resident(const typename TT::elem* __restrict__ src, int row, int N, int g,
+                                     typename TT::vec (&out)[Geo<TT, D>::DK]) {
+  using G = Geo<TT, D>;
+  using V = typename TT::vec;
+#pragma unroll
+  for (int t = 0; t < G::DK; ++t) {
+    if (row < N) {
+      out[t] = *reinterpret_cast<const V*>(src + (size_t)row * D + t * 2 * TT::KPL + g * TT::KPL);
+    } else {
+      if constexpr (TT::KPL == 1) {
+        out[t] = 0.f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < TT::KPL; ++s) out[t][s] = TT::cvt(0.f);
+      }
+    }
+  }
+}
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Store 4 consecutive head dims [dim, dim + 4) of one row.
+template <class TT>
+__device__ inline void store4(typename TT::elem* dst, float a, float b, float c, float d) {
+  using T = typename TT::elem;
+  if constexpr (sizeof(T) == 2) {
+    T v[4] = {TT::cvt(a), TT::cvt(b), TT::cvt(c), TT::cvt(d)};
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(v);
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+  }
+}
+
+template <class TT>
+__device__ inline void load4(const typename TT::elem* src, float (&o)[4]) {
+  using T = typename TT::elem;
+  if constexpr (sizeof(T) == 2) {
+    uint2 raw = *reinterpret_cast<const uint2*>(src);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = TT::tof(v[e]);
+  } else {
+    f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v[e];
+  }
+}
+
+}  // namespace fb

@@ -1,0 +1,77 @@
+// Launch interfaces between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fb {
+
+constexpr int kBlock = 256;     // 4 waves per workgroup
+constexpr int kBlockRows = 128; // resident rows per workgroup (32 per wave)
+
+enum class DT { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Statistics kernel: O, L (natural-log row LSE) and optionally D = rowsum(dO * O).
+struct FwdArgs {
+  const void *Q, *K, *V, *dO;
+  void* O;
+  float* L;
+  float* D;  // null: skip D
+  float tau;
+  int N;
+};
+
+// Pass 1 (query-tile parallel): gQ, gdO, alpha, E; or per-split partials.
+struct Pass1Args {
+  const void *Q, *K, *V, *dO, *UQ, *UK, *UV, *O;
+  const float *L, *D;
+  void *gQ, *gdO;
+  float *alpha, *E;
+  float* part;  // split records (nsplit > 1)
+  float tau;
+  int N, BH, nsplit;
+};
+
+// Pass 2 (key-tile parallel): gK, gV; or per-split partials.
+struct Pass2Args {
+  const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
+  const float *L, *D, *alpha, *E;
+  void *gK, *gV;
+  float* part;
+  float tau;
+  int N, BH, nsplit;
+};
+
+// First backward: D = rowsum(dO * O), then dQ (query-parallel) and dK, dV (key-parallel).
+struct BwdArgs {
+  const void *Q, *K, *V, *O, *dO;
+  const float* L;
+  float* D;
+  void *dQ, *dK, *dV;
+  float tau;
+  int N;
+};
+
+// Float count of one wave's partial record.
+__host__ __device__ inline size_t pass1_record_floats(int d) { return (size_t)(4 * (d / 32) * 16 + 2) * 64; }
+__host__ __device__ inline size_t pass2_record_floats(int d) { return (size_t)(2 * (d / 32) * 16) * 64; }
+__host__ __device__ inline int row_tiles(int N) { return (N + kBlockRows - 1) / kBlockRows; }
+
+// Kernels whose dynamic LDS exceeds 64 KiB must opt in (gfx950 has 160 KiB per CU).
+template <class K>
+inline hipError_t ensure_lds(K* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
+hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s);
+hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
+hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
+hipError_t launch_pass2_reduce(const Pass2Args& a, DT dt, int d, hipStream_t s);
+hipError_t launch_bwd_rowdot(const BwdArgs& a, DT dt, int d, int BH, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
+
+}  // namespace fb

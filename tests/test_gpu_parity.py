@@ -1,0 +1,277 @@
+"""HIP path against the fp64 oracle on the same seeded, dtype-rounded inputs.
+
+Bar: max over outputs of ||X_gpu - X_ref||_F / ||X_ref||_F <= 1e-4 for float32
+inputs and <= 2e-2 for bfloat16/float16 inputs. Every call goes through the
+C ABI (via the ctypes binding)."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from workload import to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp16": 2e-2}
+OUTS = ("gQ", "gK", "gV", "gdO")
+
+
+def _fb():
+    import aware_flashbob_pass_amd as fb
+
+    fb.load_library()
+    return fb
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    if nb == 0.0:
+        return float(np.max(np.abs(a))) if a.size else 0.0
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def call_errors(got, ref, keys=OUTS):
+    """Relative Frobenius error per output. An output whose exact value is zero
+    (N = 1 gives gQ = gK = gV = 0 through cancelling terms) is measured on the
+    scale of the largest output of the same call instead of its own zero norm."""
+    scale = max(float(np.linalg.norm(ref[k])) for k in keys)
+    out = {}
+    for k in keys:
+        nb = float(np.linalg.norm(ref[k]))
+        den = nb if nb > 0.0 else scale
+        out[k] = float(np.linalg.norm(np.asarray(got[k], np.float64) - ref[k]) / den) if den > 0 else 0.0
+    return out
+
+
+def _gpu_inputs(w, seed):
+    cpu = workload.make_inputs(w, seed)
+    return cpu, {k: v.cuda() for k, v in cpu.items()}
+
+
+def _run_bob(fb, g, w, **kw):
+    return fb.bob_attention(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale,
+                            causal=w.causal, **kw)
+
+
+def _oracle_full(cpu, w, heads=None):
+    arrs = [to_f64(cpu[n]) for n in workload.INPUT_NAMES]
+    if heads is not None:
+        arrs = [a.reshape(-1, w.N, w.d)[heads][None] for a in arrs]
+    return oracle.bob(*arrs, w.scale, w.causal)
+
+
+def _check_full(w, seed=0, splits=None):
+    fb = _fb()
+    _note(f"case {w.describe()} seed={seed} splits={splits}")
+    cpu, g = _gpu_inputs(w, seed)
+    if splits:
+        fb.set_tuning(*splits)
+    try:
+        out = _run_bob(fb, g, w)
+        torch.cuda.synchronize()
+    finally:
+        if splits:
+            fb.set_tuning(0, 0)
+    ref = _oracle_full(cpu, w)
+    errs = call_errors({k: to_f64(o.cpu()) for k, o in zip(OUTS, out)}, ref)
+    assert max(errs.values()) <= TOL[w.dtype], f"{w.describe()}: {errs}"
+    return errs, out
+
+
+SMALL_N = [1, 17, 64, 255, 256, 257, 1000]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_bob_bf16_sizes(N, d, causal):
+    _check_full(workload.custom(2, 2, N, d, "bf16", causal))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,N", [(64, 1), (64, 17), (64, 257), (128, 100), (64, 1000)])
+def test_bob_other_dtypes(dtype, causal, d, N):
+    _check_full(workload.custom(1, 2, N, d, dtype, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [(1, 1), (2, 3), (5, 8), (64, 64)])
+def test_bob_splits(splits, causal):
+    _check_full(workload.custom(1, 2, 1000, 64, "bf16", causal), splits=splits)
+
+
+def test_bob_splits_fp32_tight():
+    # fp32 path with several splits stays at the fp32 bar
+    _check_full(workload.custom(1, 1, 700, 64, "fp32", True), splits=(3, 4))
+
+
+def test_bob_deterministic():
+    fb = _fb()
+    w = workload.custom(1, 2, 777, 64, "bf16", False)
+    _, g = _gpu_inputs(w, 3)
+    a = _run_bob(fb, g, w)
+    b = _run_bob(fb, g, w)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bob_outputs_fully_written_and_bounded():
+    """Outputs pre-filled with NaN come back finite; guard bands around them are untouched."""
+    fb = _fb()
+    w = workload.custom(1, 3, 333, 64, "bf16", True)
+    _, g = _gpu_inputs(w, 4)
+    numel = w.B * w.H * w.N * w.d
+    guard = 4096
+    bufs = [torch.full((numel + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    outs = []
+    for b in bufs:
+        b[guard:guard + numel] = float("nan")
+        outs.append(b[guard:guard + numel].view(w.B, w.H, w.N, w.d))
+    _run_bob(fb, g, w, out=outs)
+    torch.cuda.synchronize()
+    for b, o in zip(bufs, outs):
+        assert torch.isfinite(o).all()
+        assert (b[:guard] == 7.0).all() and (b[guard + numel:] == 7.0).all()
+
+
+def test_bob_alloc_entry_point_matches_ws():
+    fb = _fb()
+    w = workload.custom(2, 1, 300, 64, "bf16", False)
+    _, g = _gpu_inputs(w, 5)
+    a = _run_bob(fb, g, w)
+    b = fb.bob_attention_alloc(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale,
+                               causal=w.causal)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("fp32", 64, False), ("bf16", 64, True), ("bf16", 128, False),
+                                            ("fp16", 64, True)])
+def test_attn_fwd_stats(dtype, d, causal):
+    fb = _fb()
+    w = workload.custom(1, 2, 300, d, dtype, causal)
+    cpu, g = _gpu_inputs(w, 6)
+    o, lse, dvec = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=causal, do=g["dO"])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), w.scale, causal)
+    _, _, _, d_ref = oracle.first_backward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), to_f64(cpu["dO"]),
+                                           w.scale, causal)
+    tol = TOL[dtype]
+    assert rel(to_f64(o.cpu()), o_ref) <= tol
+    assert rel(lse.cpu().double().numpy(), l_ref) <= (1e-6 if dtype == "fp32" else 1e-3)
+    assert rel(dvec.cpu().double().numpy(), d_ref) <= tol
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("fp32", 64, False), ("fp32", 128, True), ("bf16", 64, True),
+                                            ("bf16", 128, False), ("fp16", 64, False)])
+def test_attn_bwd(dtype, d, causal):
+    fb = _fb()
+    w = workload.custom(1, 2, 290, d, dtype, causal)
+    cpu, g = _gpu_inputs(w, 7)
+    o, lse = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=causal)
+    dq, dk, dv, dvec = fb.attn_bwd(g["Q"], g["K"], g["V"], o, g["dO"], lse, tau=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.first_backward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), to_f64(cpu["dO"]),
+                                w.scale, causal)
+    for got, exp in zip((dq, dk, dv, dvec), ref):
+        assert rel(to_f64(got.cpu()), exp) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_with_stats_row_scalars(dtype):
+    """alpha and E (the two row scalars that cross the pass boundary) against the oracle's."""
+    fb = _fb()
+    w = workload.custom(1, 2, 400, 64, dtype, True)
+    cpu, g = _gpu_inputs(w, 8)
+    o, lse, dvec = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=True, do=g["dO"])
+    outs, (alpha, e_row) = fb.bob_attention_with_stats(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], o,
+                                                       lse, dvec, tau=w.scale, causal=True, return_scalars=True)
+    torch.cuda.synchronize()
+    ref = _oracle_full(cpu, w)
+    tol = TOL[dtype]
+    assert rel(alpha.cpu().double().numpy(), ref["alpha"]) <= tol
+    assert rel(e_row.cpu().double().numpy(), ref["E"]) <= tol
+    for k, x in zip(OUTS, outs):
+        assert rel(to_f64(x.cpu()), ref[k]) <= tol
+
+
+# ---- the five workload shapes ------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_workload_tiny_fp32(seed):
+    _check_full(workload.WORKLOADS["tiny_fp32"], seed)
+
+
+def test_workload_gpt2_hessian_sampled_heads():
+    """B=8, H=12, N=1024, causal, bf16: 16 of the 96 heads against the full oracle."""
+    fb = _fb()
+    w = workload.WORKLOADS["gpt2_hessian"]
+    _note(f"case {w.describe()}")
+    cpu, g = _gpu_inputs(w, 0)
+    out = _run_bob(fb, g, w)
+    torch.cuda.synchronize()
+    heads = np.arange(0, w.B * w.H, 6)
+    ref = _oracle_full(cpu, w, heads=heads)
+    for k, o in zip(OUTS, out):
+        got = to_f64(o.cpu()).reshape(-1, w.N, w.d)[heads]
+        e = rel(got, ref[k][0])
+        assert e <= TOL[w.dtype], (k, e)
+
+
+def _rows_cols_check(w, seed, n_rows, n_cols, col_sum_tol=2e-2):
+    fb = _fb()
+    _note(f"case {w.describe()} seed={seed}")
+    cpu, g = _gpu_inputs(w, seed)
+    out = _run_bob(fb, g, w)
+    torch.cuda.synchronize()
+    del g
+    rng = np.random.default_rng(1000 + seed)
+    outs = {k: o for k, o in zip(OUTS, out)}
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        arrs = [to_f64(cpu[n][b, h]) for n in workload.INPUT_NAMES]
+        rows = np.sort(rng.choice(w.N, n_rows, replace=False))
+        rows = np.unique(np.concatenate([rows, [0, w.N - 1]]))
+        r = oracle.bob_rows_head(*arrs, w.scale, w.causal, rows)
+        for k in ("gQ", "gdO"):
+            got = outs[k][b, h, torch.as_tensor(rows, device=outs[k].device)].double().cpu().numpy()
+            e = rel(got, r[k])
+            assert e <= TOL[w.dtype], (k, bh, e)
+        if n_cols:
+            cols = np.unique(np.concatenate([np.sort(rng.choice(w.N, n_cols, replace=False)), [0, w.N - 1]]))
+            c = oracle.bob_cols_head(*arrs, w.scale, w.causal, cols, row_block=512)
+            for k in ("gK", "gV"):
+                got = outs[k][b, h, torch.as_tensor(cols, device=outs[k].device)].double().cpu().numpy()
+                e = rel(got, c[k])
+                assert e <= TOL[w.dtype], (k, bh, e)
+        # any size: the key and value cotangents sum to zero over keys
+        for k in ("gK", "gV"):
+            x = outs[k][b, h].double()
+            ratio = float(x.sum(0).norm() / x.norm())
+            assert ratio <= col_sum_tol, (k, bh, ratio)
+
+
+def test_workload_long_16k():
+    _rows_cols_check(workload.WORKLOADS["long_16k"], 0, 96, 48)
+
+
+def test_workload_wide_64k():
+    _rows_cols_check(workload.WORKLOADS["wide_64k"], 0, 32, 0)
+
+
+def test_workload_endpoint_256k():
+    _rows_cols_check(workload.WORKLOADS["endpoint_256k"], 0, 32, 0)
