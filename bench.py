@@ -1,0 +1,263 @@
+"""Benchmark of exact backward-over-backward (BoB) attention on one MI355X.
+
+One step = one whole BoB call (statistics kernel, pass 1, pass 2 and the split
+reductions) over one batch of synthetic inputs already resident in HBM.
+Default workload: one long head, B=1, H=1, N=16384, d=64, bf16, non-causal,
+tau = 1/sqrt(d), all seven inputs i.i.d. N(0, 1) from seed 0.
+
+FLOP model: one unit = one N x N x d contraction = 2 B H d n_pairs flops
+(n_pairs = N^2, or N(N+1)/2 causal). The executed schedule is 21 units
+(statistics 2 + pass 1 11 + pass 2 8); the materialised minimum is 12 units.
+`value` is TFLOP/s on the executed 21 units; MFMA utilisation is that over the
+bf16 dense peak (2.5 PFLOP/s).
+
+Prints ONE JSON line (rank 0, one GPU). `--gpus` above 1 exits: this build
+runs on one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BoB ms/call + TFLOP/s (MFMA util) at N=16K,d=64 bf16; max N on 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12}
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
+
+
+def flop_unit(w):
+    pairs = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
+    return 2.0 * w.B * w.H * w.d * pairs
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pass1_source_hash():
+    h = hashlib.sha256()
+    for f in ("bob_pass1.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "aware_flashbob_pass_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per pass-1 launch from the committed rocprofv3 counter summary,
+    or None when the summary is missing or was taken from other kernel source."""
+    try:
+        with open(PMC_SUMMARY) as fh:
+            s = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if s.get("source_hash") != pass1_source_hash():
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: query rows [0, R) of head 0 against all N keys; extrapolate by N/R."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from workload import INPUT_NAMES, to_f64
+
+    arrs = [to_f64(inputs[n][0, 0]) for n in INPUT_NAMES]
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    rows = 256
+    spent = 0.0
+    t_per_row = None
+    while True:
+        t0 = time.perf_counter()
+        oracle.bob_head(*arrs, w.scale, w.causal, row_block=256, row_range=(0, rows))
+        dt = time.perf_counter() - t0
+        spent += dt
+        t_per_row = dt / rows
+        if dt >= budget_s / 3 or rows >= w.N or spent >= budget_s:
+            break
+        rows = min(w.N, max(rows * 2, int(rows * (budget_s / 3) / max(dt, 1e-3))))
+        rows = max(256, (rows // 256) * 256)
+    full_s = t_per_row * w.N * w.B * w.H
+    # causal rows do not get cheaper in the materialised oracle (it masks, it does not skip)
+    tflops = UNITS["exec"] * flop_unit(w) / full_s / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "ms_per_call": full_s * 1e3,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 oracle on query rows 0..{rows - 1} of head 0 against all {w.N} keys "
+                  f"({dt:.1f} s), time scaled by {w.N * w.B * w.H}/{rows} rows; same 21-unit FLOP model",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_16k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-endpoint", action="store_true", help="skip the N=262144 feasibility call")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the BoB path here is single-GPU; sharding is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import aware_flashbob_pass_amd as fb
+    import workload
+
+    fb.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4, "launches": 5}))
+        return
+    w = workload.WORKLOADS[args.workload]
+    log(f"bench: {w.describe()} steps={args.steps} warmup={args.warmup}")
+    cpu_in = workload.make_inputs(w, args.seed)
+    g = {k: v.to(dev) for k, v in cpu_in.items()}
+    ws = torch.empty(max(1, fb.workspace_bytes(w.B, w.H, w.N, w.d, w.torch_dtype)), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(g["Q"]) for _ in range(4)]
+
+    def step():
+        fb.bob_attention(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale, causal=w.causal,
+                         workspace=ws, out=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    # timed region: whole-call time with stream events; per-kernel HIP events from the library
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    fb.profile_start()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kernels = fb.profile_stop()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    log(f"bench: {ms:.4f} ms/call")
+
+    # the same calls without per-kernel events, for the clean call time
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_clean = start.elapsed_time(stop) / args.steps
+
+    unit = flop_unit(w)
+    tflops = UNITS["exec"] * unit / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kern = {k: {"launches": n, "avg_ms": t / max(n, 1)} for k, (n, t) in kernels.items()}
+    p1 = kern.get("bob_pass1", {"avg_ms": float("nan")})
+    p1_flops = UNITS["pass1"] * unit
+    p1_tflops = p1_flops / (p1["avg_ms"] * 1e-3) / 1e12
+    traffic = traffic_from_profile()
+    roofline = {"bound": "mfma", "kernel": "bob_pass1", "achieved": round(p1_tflops, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(p1_tflops / peak, 5), "traffic": traffic,
+                "algorithmic_flops_per_launch": p1_flops, "avg_launch_ms": p1["avg_ms"]}
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "tau": w.scale, "seed": args.seed},
+        "roofline": roofline,
+        "mfma_util": round(tflops / peak, 5),
+        "ms_per_call_no_kernel_events": round(ms_clean, 5),
+        "tflops_useful_12_units": round(UNITS["useful"] * unit / (ms * 1e-3) / 1e12, 3),
+        "kernels": kern,
+        "peak_mem_bytes": int(torch.cuda.max_memory_allocated(dev)),
+    }
+
+    if not args.no_parity:
+        import oracle
+
+        rng = np.random.default_rng(123)
+        rows = np.unique(np.concatenate([rng.choice(w.N, 32, replace=False), [0, w.N - 1]]))
+        arrs = [workload.to_f64(cpu_in[n][0, 0]) for n in workload.INPUT_NAMES]
+        r = oracle.bob_rows_head(*arrs, w.scale, w.causal, rows)
+        errs = {}
+        for name, o in (("gQ", outs[0]), ("gdO", outs[3])):
+            got = o[0, 0, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+            errs[name] = float(np.linalg.norm(got - r[name]) / np.linalg.norm(r[name]))
+        result["parity_sampled_rows"] = {k: round(v, 6) for k, v in errs.items()}
+
+    if not args.no_endpoint:
+        we = workload.WORKLOADS["endpoint_256k"]
+        log(f"bench: feasibility call {we.describe()}")
+        del g, ws, outs
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        ge = {k: v.to(dev) for k, v in workload.make_inputs(we, args.seed).items()}
+        out_e = fb.bob_attention(*[ge[n] for n in workload.INPUT_NAMES], tau=we.scale, causal=we.causal)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out_e = fb.bob_attention(*[ge[n] for n in workload.INPUT_NAMES], tau=we.scale, causal=we.causal)
+        torch.cuda.synchronize()
+        te = time.perf_counter() - t0
+        finite = all(bool(torch.isfinite(o).all()) for o in out_e)
+        free, total = torch.cuda.mem_get_info(dev)
+        per_row = (fb.workspace_bytes(1, 1, we.N, we.d, we.torch_dtype) + 11 * we.N * we.d * 2) / we.N
+        result["max_n"] = {
+            "ran_n": we.N, "ran_ms": round(te * 1e3, 2), "finite": finite,
+            "tflops": round(UNITS["exec"] * flop_unit(we) / te / 1e12, 2),
+            "peak_mem_bytes": int(torch.cuda.max_memory_allocated(dev)),
+            "mem_bound_n_estimate": int(total / per_row),
+        }
+        del ge, out_e
+
+    if not args.no_cpu:
+        log("bench: cpu baseline (fp64 oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(w, cpu_in, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

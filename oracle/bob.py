@@ -161,7 +161,7 @@ def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1):
     }
 
 
-def bob_head(q, k, v, do, uq, uk, uv, tau, causal=False, row_block=None):
+def bob_head(q, k, v, do, uq, uk, uv, tau, causal=False, row_block=None, row_range=None):
     """BoB of one head: returns dict with gQ, gK, gV, gdO (N, d) and the row
     scalars L, D, alpha, E (N,).
 
@@ -170,16 +170,20 @@ def bob_head(q, k, v, do, uq, uk, uv, tau, causal=False, row_block=None):
     backward (review page, Summary and Strengths, Prop. 4.1).
     row_block=None evaluates all N rows at once (full N x N materialisation);
     an integer evaluates the same formulas on row blocks of that height.
+    row_range=(r0, r1) evaluates only the query rows r0..r1-1: their row outputs
+    and scalars are exact, gK and gV hold only those rows' contributions, and
+    the other rows stay zero (a bounded sample of the whole computation).
     """
     n, d = q.shape
     rb = n if row_block is None else max(1, int(row_block))
+    lo, hi = (0, n) if row_range is None else (max(0, int(row_range[0])), min(n, int(row_range[1])))
     g_q = np.zeros((n, d))
     g_do = np.zeros((n, d))
     g_k = np.zeros((n, d))
     g_v = np.zeros((n, d))
     scal = {name: np.zeros(n) for name in ("L", "D", "alpha", "E")}
-    for r0 in range(0, n, rb):
-        r1 = min(n, r0 + rb)
+    for r0 in range(lo, hi, rb):
+        r1 = min(hi, r0 + rb)
         t = _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1)
         g_q[r0:r1] = t["gQ"]
         g_do[r0:r1] = t["gdO"]
