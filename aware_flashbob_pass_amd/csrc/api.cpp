@@ -130,7 +130,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
   size_t o, l, dd, alpha, e, part, total;
-  int s1, s2;
+  int s0, s1, s2;  // splits of the statistics kernel, pass 1, pass 2
 };
 
 WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
@@ -138,6 +138,7 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   const size_t BH = (size_t)B * H;
   const size_t vec = align256(BH * N * sizeof(float));
   splits_for((int)BH, N, &w.s1, &w.s2);
+  w.s0 = dtype == FB_F32 ? 1 : w.s1;  // the float32 statistics kernel does not split
   size_t off = 0;
   w.o = off;
   off += align256(BH * N * d * esize(dtype));
@@ -152,8 +153,9 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
   const size_t p1 = w.s1 > 1 ? (size_t)w.s1 * tiles * fb::pass1_record_floats(d) * sizeof(float) : 0;
   const size_t p2 = w.s2 > 1 ? (size_t)w.s2 * tiles * fb::pass2_record_floats(d) * sizeof(float) : 0;
-  w.part = off;  // pass-1 records are consumed before pass 2 writes its own
-  off += align256(std::max(p1, p2));
+  const size_t p0 = w.s0 > 1 ? (size_t)w.s0 * tiles * fb::fwd_record_floats(d) * sizeof(float) : 0;
+  w.part = off;  // each kernel's records are consumed before the next kernel writes its own
+  off += align256(std::max(p0, std::max(p1, p2)));
   w.total = off;
   return w;
 }
@@ -239,9 +241,13 @@ fb_status_t bob_attention_ws(const void* Q, const void* K, const void* V, const 
   void* O = wsb + w.o;
   float* L = reinterpret_cast<float*>(wsb + w.l);
   float* D = reinterpret_cast<float*>(wsb + w.dd);
-  fb::FwdArgs fa{Q, K, V, dO, O, L, D, tau, N};
+  fb::FwdArgs fa{Q, K, V, dO, O, L, D, tau, N, B * H, w.s0, reinterpret_cast<float*>(wsb + w.part)};
   st = run("attn_fwd_stats", stream, [&] { return fb::launch_attn_fwd(fa, to_dt(dtype), d, causal != 0, B * H, stream); });
   if (st) return st;
+  if (w.s0 > 1) {
+    st = run("attn_fwd_combine", stream, [&] { return fb::launch_attn_fwd_combine(fa, to_dt(dtype), d, stream); });
+    if (st) return st;
+  }
   st = two_pass(Q, K, V, dO, UQ, UK, UV, O, L, D, tau, causal != 0, B, H, N, d, dtype, gQ, gK, gV, gdO,
                 reinterpret_cast<float*>(wsb + w.alpha), reinterpret_cast<float*>(wsb + w.e), wsb, w, stream);
   if (st) return st;

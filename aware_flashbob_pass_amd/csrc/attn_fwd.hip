@@ -11,8 +11,204 @@
 
 namespace fb {
 
+// O, L and (optionally) D of one wave from its unnormalised O^T accumulators,
+// running max m (log2 units, equal in lanes n and n + 32) and per-lane partial
+// denominators l.
+template <class TT, int D, bool WITH_D>
+__device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m, float l, int qi, int g, int bh,
+                                    const FwdArgs& a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  const int N = a.N;
+  const size_t base = (size_t)bh * N * D;
+  const float lt = l + xor32(l);
+  const float inv = 1.f / lt;
+  if (qi >= N) return;
+  T* O = reinterpret_cast<T*>(a.O) + base + (size_t)qi * D;
+  const T* dO = WITH_D ? reinterpret_cast<const T*>(a.dO) + base + (size_t)qi * D : nullptr;
+  float dot = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = mb * 32 + kappa(r4 * 4, g);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[mb][r4 * 4 + e] * inv;
+      store4<TT>(O + dim, o[0], o[1], o[2], o[3]);
+      if constexpr (WITH_D) {
+        float x[4];
+        load4<TT>(dO + dim, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot += x[e] * o[e];
+      }
+    }
+  // lanes n and n + 32 own the same query, so the exchange stays paired
+  if (g == 0) a.L[(size_t)bh * N + qi] = m * kLn2 + __logf(lt);
+  if constexpr (WITH_D) {
+    dot += xor32(dot);
+    if (g == 0) a.D[(size_t)bh * N + qi] = dot;
+  }
+}
+
+// Pipelined variant for 16-bit inputs (same staging scheme as pass 1): K and V
+// tiles in three row-major LDS stages prefetched two steps ahead; the next
+// step's score tile is formed while the current one goes through the online
+// softmax; P V reads V^T operands with the transposing LDS load. The running
+// rescale of the accumulators is skipped when no row maximum of the wave grew.
+// With `nsplit` > 1 each split covers a key range and writes a record
+// (accumulators, max, partial denominators) that fwd_combine merges.
 template <class TT, int D, bool CAUSAL, bool WITH_D>
-__global__ __launch_bounds__(kBlock) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  using V = typename TT::vec;
+  constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
+  constexpr int NT = 2, NBUF = 3;
+  static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  const size_t base = (size_t)bh * N * D;
+  const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base};
+  const int q0 = blockIdx.x * kBlockRows + wave * kTile;
+  const int qi = q0 + n;
+
+  V bq[DK];
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+  float m = -1e30f, l = 0.f;
+  const float cs = a.tau * kLog2e;
+
+  int nkt = (N + kTile - 1) / kTile;
+  if (CAUSAL) nkt = min(nkt, (int)(blockIdx.x + 1) * (kBlockRows / kTile));
+  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
+  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
+  const int nsteps = kt_end - kt_begin;
+  auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
+  auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
+
+  StagePrefetch<TT, D, NT, kBlock> pf;
+  for (int j = 0; j < 2 && j < nsteps; ++j) {
+    pf.load(src, (kt_begin + j) * kTile, N, tid);
+    T* dst[NT] = {stage(j, 0), stage(j, 1)};
+    pf.commit(dst, tid);
+  }
+  if (nsteps > 2) pf.load(src, (kt_begin + 2) * kTile, N, tid);
+  __syncthreads();
+
+  f32x16 sc = zero16();
+  if (nsteps > 0 && active(0)) {
+#pragma unroll
+    for (int t = 0; t < DK; ++t) sc = TT::mfma(lds_row_op<TT, D>(stage(0, 0), n, t, g), bq[t], sc);
+  }
+  for (int j = 0; j < nsteps; ++j) {
+    if (j + 2 < nsteps) {
+      T* dst[NT] = {stage(j + 2, 0), stage(j + 2, 1)};
+      pf.commit(dst, tid);
+    }
+    if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
+    const bool act = active(j);
+    const bool act_next = (j + 1 < nsteps) && active(j + 1);
+    const int k0 = (kt_begin + j) * kTile;
+    f32x16 sx = zero16();
+    if (act) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] *= cs;
+      if (k0 + kTile > N || (CAUSAL && k0 + kTile - 1 > q0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kappa(r, g);
+          if (!(key < N && (!CAUSAL || key <= qi))) sc[r] = -INFINITY;
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float mnew = fmaxf(m, mx);
+      if (__ballot(mnew > m)) {
+        const float f = fast_exp2(m - mnew);
+        l *= f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] *= f;
+        m = mnew;
+      }
+      V pp[NK];
+#pragma unroll
+      for (int t = 0; t < DK; ++t) {
+        if (act_next) sx = TT::mfma(lds_row_op<TT, D>(stage(j + 1, 0), n, t, g), bq[t], sx);
+#pragma unroll
+        for (int r = t * 16 / DK; r < (t + 1) * 16 / DK; ++r) {
+          const float p = fast_exp2(sc[r] - m);
+          l += p;
+          vset<TT>(pp[r >> 3], r & 7, p);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = TT::mfma(lds_tr_op<TT, D>(stage(j, 1), mb, t, lane), pp[t], acc[mb]);
+    } else if (act_next) {
+#pragma unroll
+      for (int t = 0; t < DK; ++t) sx = TT::mfma(lds_row_op<TT, D>(stage(j + 1, 0), n, t, g), bq[t], sx);
+    }
+    sc = sx;
+    __syncthreads();
+  }
+
+  if (a.nsplit == 1) {
+    fwd_epilogue<TT, D, WITH_D>(acc, m, l, qi, g, bh, a);
+    return;
+  }
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + blockIdx.x) * 4 + wave;
+  float* R = a.part + rec * fwd_record_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) R[(mb * 16 + r) * 64 + lane] = acc[mb][r];
+  R[MB * 16 * 64 + lane] = m;
+  R[MB * 16 * 64 + 64 + lane] = l;
+}
+
+// Merge the split records of each wave (fixed split order) and apply the epilogue.
+template <class TT, int D, bool WITH_D>
+__global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
+  using G = Geo<TT, D>;
+  constexpr int MB = G::MB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int bh = blockIdx.y;
+  const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
+  auto rec = [&](int sp) {
+    return a.part + ((((size_t)sp * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave) * fwd_record_floats(D);
+  };
+  float M = -1e30f;
+  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, rec(sp)[MB * 16 * 64 + lane]);
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+  float l = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* R = rec(sp);
+    const float w = fast_exp2(R[MB * 16 * 64 + lane] - M);
+    l += w * R[MB * 16 * 64 + 64 + lane];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][r] += w * R[(mb * 16 + r) * 64 + lane];
+  }
+  fwd_epilogue<TT, D, WITH_D>(acc, M, l, qi, g, bh, a);
+}
+
+// Single-buffered variant (transposed LDS copy of V); used for float32 inputs.
+template <class TT, int D, bool CAUSAL, bool WITH_D>
+__global__ __launch_bounds__(kBlock) void attn_fwd_simple_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
@@ -114,11 +310,19 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_kernel(FwdArgs a) {
 template <class TT, int D, bool CAUSAL, bool WITH_D>
 static hipError_t launch_fwd_t(const FwdArgs& a, int BH, hipStream_t s) {
   using G = Geo<TT, D>;
-  const size_t lds = (size_t)(G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
-  hipError_t e = ensure_lds(&attn_fwd_kernel<TT, D, CAUSAL, WITH_D>, lds);
-  if (e != hipSuccess) return e;
-  dim3 grid(row_tiles(a.N), BH);
-  hipLaunchKernelGGL((attn_fwd_kernel<TT, D, CAUSAL, WITH_D>), grid, dim3(kBlock), lds, s, a);
+  if constexpr (TT::KPL == 1) {
+    const size_t lds = (size_t)(G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
+    hipError_t e = ensure_lds(&attn_fwd_simple_kernel<TT, D, CAUSAL, WITH_D>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_fwd_simple_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH), dim3(kBlock), lds,
+                       s, a);
+  } else {
+    const size_t lds = (size_t)3 * 2 * G::ROW_ELEMS * sizeof(typename TT::elem);
+    hipError_t e = ensure_lds(&attn_fwd_kernel<TT, D, CAUSAL, WITH_D>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_fwd_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH, a.nsplit), dim3(kBlock),
+                       lds, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -135,10 +339,30 @@ static hipError_t launch_fwd_tt(const FwdArgs& a, int d, bool causal, int BH, hi
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s) {
+  if (dt == DT::F32 && a.nsplit != 1) return hipErrorInvalidValue;
   switch (dt) {
     case DT::BF16: return launch_fwd_tt<BF16>(a, d, causal, BH, s);
     case DT::F16: return launch_fwd_tt<F16>(a, d, causal, BH, s);
     default: return launch_fwd_tt<F32>(a, d, causal, BH, s);
+  }
+}
+
+template <class TT, int D>
+static hipError_t launch_fc_t(const FwdArgs& a, hipStream_t s) {
+  dim3 grid(row_tiles(a.N), a.BH);
+  if (a.D) {
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<TT, D, true>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<TT, D, false>), grid, dim3(kBlock), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_combine(const FwdArgs& a, DT dt, int d, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return d == 64 ? launch_fc_t<BF16, 64>(a, s) : launch_fc_t<BF16, 128>(a, s);
+    case DT::F16: return d == 64 ? launch_fc_t<F16, 64>(a, s) : launch_fc_t<F16, 128>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

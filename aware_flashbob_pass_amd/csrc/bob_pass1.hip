@@ -74,8 +74,32 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[Geo<TT, D>::MB], const f
   }
 }
 
+
+// Raw accumulators and row partials of one wave for split `split`.
+template <class TT, int D>
+__device__ inline void pass1_write_record(const f32x16 (&A)[Geo<TT, D>::MB], const f32x16 (&B)[Geo<TT, D>::MB],
+                                          const f32x16 (&C)[Geo<TT, D>::MB], const f32x16 (&X)[Geo<TT, D>::MB],
+                                          float alpha_p, float e0_p, int split, int bh, int wave, int lane,
+                                          const Pass1Args& a) {
+  constexpr int MB = Geo<TT, D>::MB;
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
+  float* R = a.part + rec * pass1_record_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      R[((0 * MB + mb) * 16 + r) * 64 + lane] = A[mb][r];
+      R[((1 * MB + mb) * 16 + r) * 64 + lane] = B[mb][r];
+      R[((2 * MB + mb) * 16 + r) * 64 + lane] = C[mb][r];
+      R[((3 * MB + mb) * 16 + r) * 64 + lane] = X[mb][r];
+    }
+  R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
+  R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;
+}
+
+// Single-buffered variant (transposed LDS copies); used for float32 inputs.
 template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBlock) void bob_pass1_kernel(Pass1Args a) {
+__global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
@@ -200,20 +224,201 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_kernel(Pass1Args a) {
     pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
     return;
   }
-  const int qt_count = row_tiles(N);
-  const size_t rec = (((size_t)split * a.BH + bh) * qt_count + blockIdx.x) * 4 + wave;
-  float* R = a.part + rec * pass1_record_floats(D);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, a);
+}
+
+// Pipelined variant for 16-bit inputs. LDS holds three stages of row-major
+// K, V, UK, UV tiles (32 keys each); the registers of every thread prefetch the
+// stage two steps ahead, so each step has a single barrier and no exposed
+// global-load latency. Within a step, the score tiles of the NEXT step are
+// formed on the matrix cores while the element-wise work of the current step
+// runs on the vector ALUs, and the accumulating contractions read their
+// transposed operands with the transposing LDS load (lds_tr_op).
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  using V = typename TT::vec;
+  constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
+  constexpr int NT = 4, NBUF = 3;
+  static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  const size_t base = (size_t)bh * N * D;
+  const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base,
+                      reinterpret_cast<const T*>(a.UK) + base, reinterpret_cast<const T*>(a.UV) + base};
+  const int q0 = blockIdx.x * kBlockRows + wave * kTile;
+  const int qi = q0 + n;
+
+  V bq[DK], bdo[DK], buq[DK];
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.dO) + base, qi, N, g, bdo);
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.UQ) + base, qi, N, g, buq);
+  const size_t rowv = (size_t)bh * N + (qi < N ? qi : 0);
+  const float lq = a.L[rowv] * kLog2e;
+  const float dq = a.D[rowv];
+  const float cs = a.tau * kLog2e;
+  const float tau = a.tau;
+
+  f32x16 accA[MB], accB[MB], accC[MB], accX[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = zero16();
+    accB[mb] = zero16();
+    accC[mb] = zero16();
+    accX[mb] = zero16();
+  }
+  float alpha_p = 0.f, e0_p = 0.f;
+
+  int nkt = (N + kTile - 1) / kTile;
+  if (CAUSAL) nkt = min(nkt, (int)(blockIdx.x + 1) * (kBlockRows / kTile));
+  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
+  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
+  const int nsteps = kt_end - kt_begin;
+
+  auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
+  auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
+
+  StagePrefetch<TT, D, NT, kBlock> pf;
+  for (int j = 0; j < 2 && j < nsteps; ++j) {
+    pf.load(src, (kt_begin + j) * kTile, N, tid);
+    T* dst[NT] = {stage(j, 0), stage(j, 1), stage(j, 2), stage(j, 3)};
+    pf.commit(dst, tid);
+  }
+  if (nsteps > 2) pf.load(src, (kt_begin + 2) * kTile, N, tid);
+  __syncthreads();
+
+  // score tiles of the current step (c) and of the next step (x)
+  f32x16 sc = zero16(), gc = zero16(), pc = zero16(), hc = zero16();
+  if (nsteps > 0 && active(0)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      R[((0 * MB + mb) * 16 + r) * 64 + lane] = accA[mb][r];
-      R[((1 * MB + mb) * 16 + r) * 64 + lane] = accB[mb][r];
-      R[((2 * MB + mb) * 16 + r) * 64 + lane] = accC[mb][r];
-      R[((3 * MB + mb) * 16 + r) * 64 + lane] = accX[mb][r];
+    for (int t = 0; t < DK; ++t) {
+      const V ak = lds_row_op<TT, D>(stage(0, 0), n, t, g);
+      const V av = lds_row_op<TT, D>(stage(0, 1), n, t, g);
+      const V auk = lds_row_op<TT, D>(stage(0, 2), n, t, g);
+      const V auv = lds_row_op<TT, D>(stage(0, 3), n, t, g);
+      sc = TT::mfma(ak, bq[t], sc);
+      gc = TT::mfma(ak, buq[t], gc);
+      gc = TT::mfma(auk, bq[t], gc);
+      pc = TT::mfma(av, bdo[t], pc);
+      hc = TT::mfma(auv, bdo[t], hc);
     }
-  R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
-  R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;
+  }
+
+  for (int j = 0; j < nsteps; ++j) {
+    if (j + 2 < nsteps) {
+      T* dst[NT] = {stage(j + 2, 0), stage(j + 2, 1), stage(j + 2, 2), stage(j + 2, 3)};
+      pf.commit(dst, tid);
+    }
+    if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
+    const bool act = active(j);
+    const bool act_next = (j + 1 < nsteps) && active(j + 1);
+    const int k0 = (kt_begin + j) * kTile;
+    f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
+
+    if (act) {
+      // log2-domain scores, masked where the key is out of range or after the query
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = sc[r] * cs - lq;
+      if (k0 + kTile > N || (CAUSAL && k0 + kTile - 1 > q0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kappa(r, g);
+          if (!(key < N && (!CAUSAL || key <= qi))) sc[r] = -INFINITY;
+        }
+      }
+      V wa[NK], wb[NK], pd[NK], pp[NK], pg[NK];
+      auto elementwise = [&](int r) {
+        const float p = fast_exp2(sc[r]);
+        const float gv = gc[r] * tau;
+        const float dpv = pc[r];
+        const float t1 = dpv - dq;
+        const float vpg = p * gv;
+        const float vwb = p * fmaf(gv, t1, hc[r]);
+        alpha_p += vpg;
+        e0_p += vwb;
+        const int kk = r >> 3, ss = r & 7;
+        vset<TT>(wa[kk], ss, p * t1);
+        vset<TT>(wb[kk], ss, vwb);
+        vset<TT>(pd[kk], ss, p * dpv);
+        vset<TT>(pp[kk], ss, p);
+        vset<TT>(pg[kk], ss, vpg);
+      };
+      // phase 1: next step's score tiles (matrix cores) with rows 0..7 (vector ALUs)
+      const T* nk = stage(j + 1, 0);
+      const T* nv = stage(j + 1, 1);
+      const T* nuk = stage(j + 1, 2);
+      const T* nuv = stage(j + 1, 3);
+#pragma unroll
+      for (int t = 0; t < DK; ++t) {
+        if (act_next) {
+          const V ak = lds_row_op<TT, D>(nk, n, t, g);
+          const V av = lds_row_op<TT, D>(nv, n, t, g);
+          const V auk = lds_row_op<TT, D>(nuk, n, t, g);
+          const V auv = lds_row_op<TT, D>(nuv, n, t, g);
+          sx = TT::mfma(ak, bq[t], sx);
+          gx = TT::mfma(ak, buq[t], gx);
+          gx = TT::mfma(auk, bq[t], gx);
+          px = TT::mfma(av, bdo[t], px);
+          hx = TT::mfma(auv, bdo[t], hx);
+        }
+#pragma unroll
+        for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
+      }
+      // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
+      const T* ck = stage(j, 0);
+      const T* cv = stage(j, 1);
+      const T* cuk = stage(j, 2);
+      const T* cuv = stage(j, 3);
+#pragma unroll
+      for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const V tk = lds_tr_op<TT, D>(ck, mb, t, lane);
+          const V tuk = lds_tr_op<TT, D>(cuk, mb, t, lane);
+          const V tv = lds_tr_op<TT, D>(cv, mb, t, lane);
+          const V tuv = lds_tr_op<TT, D>(cuv, mb, t, lane);
+          if (t == 0) {
+#pragma unroll
+            for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
+          }
+          accA[mb] = TT::mfma(tuk, wa[t], accA[mb]);
+          accA[mb] = TT::mfma(tk, wb[t], accA[mb]);
+          accB[mb] = TT::mfma(tk, pd[t], accB[mb]);
+          accC[mb] = TT::mfma(tk, pp[t], accC[mb]);
+          accX[mb] = TT::mfma(tuv, pp[t], accX[mb]);
+          accX[mb] = TT::mfma(tv, pg[t], accX[mb]);
+        }
+    } else if (act_next) {
+#pragma unroll
+      for (int t = 0; t < DK; ++t) {
+        const V ak = lds_row_op<TT, D>(stage(j + 1, 0), n, t, g);
+        const V av = lds_row_op<TT, D>(stage(j + 1, 1), n, t, g);
+        const V auk = lds_row_op<TT, D>(stage(j + 1, 2), n, t, g);
+        const V auv = lds_row_op<TT, D>(stage(j + 1, 3), n, t, g);
+        sx = TT::mfma(ak, bq[t], sx);
+        gx = TT::mfma(ak, buq[t], gx);
+        gx = TT::mfma(auk, bq[t], gx);
+        px = TT::mfma(av, bdo[t], px);
+        hx = TT::mfma(auv, bdo[t], hx);
+      }
+    }
+    sc = sx;
+    gc = gx;
+    pc = px;
+    hc = hx;
+    __syncthreads();
+  }
+
+  if (a.nsplit == 1) {
+    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
+    return;
+  }
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, a);
 }
 
 // Sum the split records of each wave in split order, then apply the epilogue.
@@ -256,16 +461,23 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
 template <class TT, int D>
 static size_t pass1_lds_bytes() {
   using G = Geo<TT, D>;
-  return (size_t)4 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
+  if constexpr (TT::KPL == 1) return (size_t)4 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
+  return (size_t)3 * 4 * G::ROW_ELEMS * sizeof(typename TT::elem);
 }
 
 template <class TT, int D, bool CAUSAL>
 static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
   const size_t lds = pass1_lds_bytes<TT, D>();
-  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL>, lds);
-  if (e != hipSuccess) return e;
   dim3 grid(row_tiles(a.N), a.BH, a.nsplit);
-  hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  if constexpr (TT::KPL == 1) {
+    hipError_t e = ensure_lds(&bob_pass1_simple_kernel<TT, D, CAUSAL>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bob_pass1_simple_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  } else {
+    hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -40,8 +40,24 @@ __device__ inline void pass2_epilogue(const f32x16 (&dK)[Geo<TT, D>::MB], const 
     }
 }
 
+template <class TT, int D>
+__device__ inline void pass2_write_record(const f32x16 (&dK)[Geo<TT, D>::MB], const f32x16 (&dV)[Geo<TT, D>::MB],
+                                          int split, int bh, int wave, int lane, const Pass2Args& a) {
+  constexpr int MB = Geo<TT, D>::MB;
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
+  float* R = a.part + rec * pass2_record_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      R[((0 * MB + mb) * 16 + r) * 64 + lane] = dK[mb][r];
+      R[((1 * MB + mb) * 16 + r) * 64 + lane] = dV[mb][r];
+    }
+}
+
+// Single-buffered variant (transposed LDS copies); used for float32 inputs.
 template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBlock) void bob_pass2_kernel(Pass2Args a) {
+__global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
@@ -158,16 +174,188 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_kernel(Pass2Args a) {
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);
     return;
   }
-  const int kt_count = row_tiles(N);
-  const size_t rec = (((size_t)split * a.BH + bh) * kt_count + blockIdx.x) * 4 + wave;
-  float* R = a.part + rec * pass2_record_floats(D);
+  pass2_write_record<TT, D>(accK, accV, split, bh, wave, lane, a);
+}
+
+// Pipelined variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
+// tiles plus their four row scalars, prefetched two steps ahead; the next
+// step's score tiles are formed on the matrix cores while the current step's
+// weights are computed; transposed operands come from the transposing LDS load.
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  using V = typename TT::vec;
+  constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
+  constexpr int NT = 3, NBUF = 3;
+  constexpr int STAGE_ELEMS = NT * G::ROW_ELEMS + 4 * kTile * 4 / (int)sizeof(T);  // tiles + 4 x 32 floats
+  static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  const size_t base = (size_t)bh * N * D;
+  const size_t vbase = (size_t)bh * N;
+  const T* src[NT] = {reinterpret_cast<const T*>(a.Q) + base, reinterpret_cast<const T*>(a.dO) + base,
+                      reinterpret_cast<const T*>(a.UQ) + base};
+  const float* vsrc[4] = {a.L + vbase, a.D + vbase, a.alpha + vbase, a.E + vbase};
+  const int k0w = blockIdx.x * kBlockRows + wave * kTile;
+  const int kj = k0w + n;
+
+  V bk[DK], bv[DK], buk[DK], buv[DK];
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.K) + base, kj, N, g, bk);
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.V) + base, kj, N, g, bv);
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.UK) + base, kj, N, g, buk);
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.UV) + base, kj, N, g, buv);
+  const float cs = a.tau * kLog2e;
+  const float tau = a.tau;
+
+  f32x16 accK[MB], accV[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      R[((0 * MB + mb) * 16 + r) * 64 + lane] = accK[mb][r];
-      R[((1 * MB + mb) * 16 + r) * 64 + lane] = accV[mb][r];
+  for (int mb = 0; mb < MB; ++mb) {
+    accK[mb] = zero16();
+    accV[mb] = zero16();
+  }
+
+  const int nqt = (N + kTile - 1) / kTile;
+  const int qt_first = CAUSAL ? (int)blockIdx.x * (kBlockRows / kTile) : 0;
+  const int span = nqt - qt_first;
+  const int it_begin = qt_first + (int)((long long)split * span / a.nsplit);
+  const int it_end = qt_first + (int)((long long)(split + 1) * span / a.nsplit);
+  const int nsteps = it_end - it_begin;
+
+  auto tile = [&](int j, int t) { return lds + (j % NBUF) * STAGE_ELEMS + t * G::ROW_ELEMS; };
+  auto scal = [&](int j) { return reinterpret_cast<float*>(lds + (j % NBUF) * STAGE_ELEMS + NT * G::ROW_ELEMS); };
+  auto active = [&](int j) { return !CAUSAL || (it_begin + j) * kTile + kTile - 1 >= k0w; };
+
+  StagePrefetch<TT, D, NT, kBlock> pf;
+  float sreg = 0.f;  // one of the 4 x 32 row scalars of the prefetched stage (threads 0..127)
+  auto load_scal = [&](int i0) {
+    sreg = 0.f;
+    if (tid < 4 * kTile) {
+      const int which = tid / kTile, row = i0 + tid % kTile;
+      if (row < N) sreg = vsrc[which][row] * (which == 0 ? kLog2e : 1.f);
     }
+  };
+  auto commit = [&](int j) {
+    T* dst[NT] = {tile(j, 0), tile(j, 1), tile(j, 2)};
+    pf.commit(dst, tid);
+    if (tid < 4 * kTile) scal(j)[tid] = sreg;
+  };
+  for (int j = 0; j < 2 && j < nsteps; ++j) {
+    pf.load(src, (it_begin + j) * kTile, N, tid);
+    load_scal((it_begin + j) * kTile);
+    commit(j);
+  }
+  if (nsteps > 2) {
+    pf.load(src, (it_begin + 2) * kTile, N, tid);
+    load_scal((it_begin + 2) * kTile);
+  }
+  __syncthreads();
+
+  f32x16 sc = zero16(), gc = zero16(), pc = zero16(), hc = zero16();
+  auto scores_kstep = [&](int j, int t, f32x16& s_, f32x16& g_, f32x16& p_, f32x16& h_) {
+    const V aq = lds_row_op<TT, D>(tile(j, 0), n, t, g);
+    const V ado = lds_row_op<TT, D>(tile(j, 1), n, t, g);
+    const V auq = lds_row_op<TT, D>(tile(j, 2), n, t, g);
+    s_ = TT::mfma(aq, bk[t], s_);
+    g_ = TT::mfma(auq, bk[t], g_);
+    g_ = TT::mfma(aq, buk[t], g_);
+    p_ = TT::mfma(ado, bv[t], p_);
+    h_ = TT::mfma(ado, buv[t], h_);
+  };
+  if (nsteps > 0 && active(0)) {
+#pragma unroll
+    for (int t = 0; t < DK; ++t) scores_kstep(0, t, sc, gc, pc, hc);
+  }
+
+  for (int j = 0; j < nsteps; ++j) {
+    if (j + 2 < nsteps) commit(j + 2);
+    if (j + 3 < nsteps) {
+      pf.load(src, (it_begin + j + 3) * kTile, N, tid);
+      load_scal((it_begin + j + 3) * kTile);
+    }
+    const bool act = active(j);
+    const bool act_next = (j + 1 < nsteps) && active(j + 1);
+    const int i0 = (it_begin + j) * kTile;
+    f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
+    if (act) {
+      const float* sv = scal(j);
+      float lqv[16], dqv[16], alv[16], eqv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int q = r4 * 8 + g * 4;  // rows kappa(4 r4 .. 4 r4 + 3, g)
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sv + q);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sv + kTile + q);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sv + 2 * kTile + q);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(sv + 3 * kTile + q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lqv[r4 * 4 + e] = l4[e];
+          dqv[r4 * 4 + e] = d4[e];
+          alv[r4 * 4 + e] = a4[e];
+          eqv[r4 * 4 + e] = e4[e];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = sc[r] * cs - lqv[r];
+      if (i0 + kTile > N || (CAUSAL && i0 < k0w + kTile - 1)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + kappa(r, g);
+          if (!(qrow < N && (!CAUSAL || kj <= qrow))) sc[r] = -INFINITY;
+        }
+      }
+      V wds[NK], wsb[NK], wdp[NK];
+      auto elementwise = [&](int r) {
+        const float p = fast_exp2(sc[r]);
+        const float gv = gc[r] * tau;
+        const float dpv = pc[r];
+        const float t1 = dpv - dqv[r];
+        const int kk = r >> 3, ss = r & 7;
+        vset<TT>(wds[kk], ss, p * t1);
+        vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(alv[r], dpv, eqv[r])));
+        vset<TT>(wdp[kk], ss, p * (gv - alv[r]));
+      };
+#pragma unroll
+      for (int t = 0; t < DK; ++t) {
+        if (act_next) scores_kstep(j + 1, t, sx, gx, px, hx);
+#pragma unroll
+        for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
+      }
+#pragma unroll
+      for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const V tuq = lds_tr_op<TT, D>(tile(j, 2), mb, t, lane);
+          const V tq = lds_tr_op<TT, D>(tile(j, 0), mb, t, lane);
+          const V tdo = lds_tr_op<TT, D>(tile(j, 1), mb, t, lane);
+          if (t == 0) {
+#pragma unroll
+            for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
+          }
+          accK[mb] = TT::mfma(tuq, wds[t], accK[mb]);
+          accK[mb] = TT::mfma(tq, wsb[t], accK[mb]);
+          accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);
+        }
+    } else if (act_next) {
+#pragma unroll
+      for (int t = 0; t < DK; ++t) scores_kstep(j + 1, t, sx, gx, px, hx);
+    }
+    sc = sx;
+    gc = gx;
+    pc = px;
+    hc = hx;
+    __syncthreads();
+  }
+
+  if (a.nsplit == 1) {
+    pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);
+    return;
+  }
+  pass2_write_record<TT, D>(accK, accV, split, bh, wave, lane, a);
 }
 
 template <class TT, int D>
@@ -202,16 +390,24 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
 template <class TT, int D>
 static size_t pass2_lds_bytes() {
   using G = Geo<TT, D>;
-  return (size_t)3 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem) + 4 * kTile * sizeof(float);
+  if constexpr (TT::KPL == 1)
+    return (size_t)3 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem) + 4 * kTile * sizeof(float);
+  return (size_t)3 * (3 * G::ROW_ELEMS * sizeof(typename TT::elem) + 4 * kTile * sizeof(float));
 }
 
 template <class TT, int D, bool CAUSAL>
 static hipError_t launch_p2_t(const Pass2Args& a, hipStream_t s) {
   const size_t lds = pass2_lds_bytes<TT, D>();
-  hipError_t e = ensure_lds(&bob_pass2_kernel<TT, D, CAUSAL>, lds);
-  if (e != hipSuccess) return e;
   dim3 grid(row_tiles(a.N), a.BH, a.nsplit);
-  hipLaunchKernelGGL((bob_pass2_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  if constexpr (TT::KPL == 1) {
+    hipError_t e = ensure_lds(&bob_pass2_simple_kernel<TT, D, CAUSAL>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bob_pass2_simple_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  } else {
+    hipError_t e = ensure_lds(&bob_pass2_kernel<TT, D, CAUSAL>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bob_pass2_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+  }
   return hipGetLastError();
 }
 

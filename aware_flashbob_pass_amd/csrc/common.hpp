@@ -170,6 +170,71 @@ __device__ inline void load_resident(const typename TT::elem* __restrict__ src, 
   }
 }
 
+// ---- pipelined staging (16-bit types) -------------------------------------------
+// One stage = 32 streamed rows of NT [N][D] tensors, copied global -> registers
+// (load) one step ahead of use and registers -> row-major padded LDS (commit).
+template <class TT, int D, int NT, int NTHREADS>
+struct StagePrefetch {
+  using T = typename TT::elem;
+  static constexpr int CH = 16 / sizeof(T);
+  static constexpr int CPR = D / CH;
+  static constexpr int NCH = kTile * CPR;
+  static constexpr int PER = (NCH + NTHREADS - 1) / NTHREADS;
+  uint4 r[NT][PER];
+
+  __device__ inline void load(const T* const (&src)[NT], int r0, int N, int tid) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int c = tid + p * NTHREADS;
+        const int row = c / CPR, e0 = (c % CPR) * CH;
+        const int grow = r0 + row;
+        r[t][p] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < NCH && grow < N) r[t][p] = *reinterpret_cast<const uint4*>(src[t] + (size_t)grow * D + e0);
+      }
+  }
+  __device__ inline void commit(T* const (&dst)[NT], int tid) const {
+    using G = Geo<TT, D>;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int c = tid + p * NTHREADS;
+        if (c < NCH) {
+          const int row = c / CPR, e0 = (c % CPR) * CH;
+          *reinterpret_cast<uint4*>(dst[t] + row * G::RS + e0) = r[t][p];
+        }
+      }
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// A operand of an accumulating contraction (head dims x streamed rows) read from
+// the ROW-MAJOR copy with gfx950's transposing LDS load. Within each 16-lane
+// group, the load hands destination lane i element (i % 4) of the 8-byte chunk
+// addressed by source lane 4e + i / 4, for e = 0..3. Each lane therefore
+// addresses streamed row (base + e_src) at head dims 4 * q_src .. + 3 with
+// e_src = (lane % 16) / 4, q_src = lane % 4, and receives 4 streamed rows of
+// head dim (lane % 16) of its 16-dim group. Two loads (h = 0, 1) give the 8
+// k-slots s = 4h + e, which are streamed rows 16t + 8h + 4g + e = kappa(8t + s, g),
+// the same rows the score-tile B operand holds in its slots.
+template <class TT, int D>
+__device__ inline typename TT::vec lds_tr_op(const typename TT::elem* rowbuf, int mb, int t, int lane) {
+  using G = Geo<TT, D>;
+  static_assert(TT::KPL == 8, "transposing LDS loads are for 16-bit types");
+  const int i = lane & 15, g = lane >> 5, half = (lane >> 4) & 1;
+  const int col = mb * 32 + half * 16 + (i & 3) * 4;
+  const int row0 = t * 16 + g * 4 + (i >> 2);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + row0 * G::RS + col));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + (row0 + 8) * G::RS + col));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename TT::vec, v);
+}
+
 __device__ inline f32x16 zero16() {
   f32x16 z;
 #pragma unroll

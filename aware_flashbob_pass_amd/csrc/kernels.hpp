@@ -19,6 +19,9 @@ struct FwdArgs {
   float* D;  // null: skip D
   float tau;
   int N;
+  int BH = 1;
+  int nsplit = 1;
+  float* part = nullptr;  // split records (nsplit > 1)
 };
 
 // Pass 1 (query-tile parallel): gQ, gdO, alpha, E; or per-split partials.
@@ -54,6 +57,7 @@ struct BwdArgs {
 
 // Float count of one wave's partial record.
 __host__ __device__ inline size_t pass1_record_floats(int d) { return (size_t)(4 * (d / 32) * 16 + 2) * 64; }
+__host__ __device__ inline size_t fwd_record_floats(int d) { return (size_t)((d / 32) * 16 + 2) * 64; }
 __host__ __device__ inline size_t pass2_record_floats(int d) { return (size_t)(2 * (d / 32) * 16) * 64; }
 __host__ __device__ inline int row_tiles(int N) { return (N + kBlockRows - 1) / kBlockRows; }
 
@@ -66,6 +70,7 @@ inline hipError_t ensure_lds(K* kernel, size_t bytes) {
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
+hipError_t launch_attn_fwd_combine(const FwdArgs& a, DT dt, int d, hipStream_t s);
 hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
 hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
