@@ -6,6 +6,8 @@
 //   O = softmax(tau Q K^T) V,  L_i = log sum_j exp(tau q_i . k_j),
 // and, fused into its epilogue, D_i = sum_t dO_it O_it formed from the float32
 // O before rounding (D = rowsum(P * dP) = rowsum(dO * O) in exact arithmetic).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -107,9 +109,11 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < DK; ++t) sc = TT::mfma(lds_row_op<TT, D>(stage(0, 0), n, t, g), bq[t], sc);
   }
-  for (int j = 0; j < nsteps; ++j) {
+  auto step = [&](auto S_c, int j) {
+    constexpr int S = decltype(S_c)::value;
+    constexpr int SN = (S + 1) % NBUF, SC = (S + 2) % NBUF;
     if (j + 2 < nsteps) {
-      T* dst[NT] = {stage(j + 2, 0), stage(j + 2, 1)};
+      T* dst[NT] = {stage(SC, 0), stage(SC, 1)};
       pf.commit(dst, tid);
     }
     if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
       V pp[NK];
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        if (act_next) sx = TT::mfma(lds_row_op<TT, D>(stage(j + 1, 0), n, t, g), bq[t], sx);
+        sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);  // stale on the last step
 #pragma unroll
         for (int r = t * 16 / DK; r < (t + 1) * 16 / DK; ++r) {
           const float p = fast_exp2(sc[r] - m);
@@ -153,14 +157,25 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NK; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = TT::mfma(lds_tr_op<TT, D>(stage(j, 1), mb, t, lane), pp[t], acc[mb]);
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = TT::mfma(lds_tr_op<TT, D>(stage(S, 1), mb, t, lane), pp[t], acc[mb]);
     } else if (act_next) {
 #pragma unroll
-      for (int t = 0; t < DK; ++t) sx = TT::mfma(lds_row_op<TT, D>(stage(j + 1, 0), n, t, g), bq[t], sx);
+      for (int t = 0; t < DK; ++t) sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);
     }
     sc = sx;
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int j = 0;
+  for (; j + NBUF <= nsteps; j += NBUF) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
+    step(I2{}, j + 2);
   }
+  if (j < nsteps) step(I0{}, j);
+  if (j + 1 < nsteps) step(I1{}, j + 1);
 
   if (a.nsplit == 1) {
     fwd_epilogue<TT, D, WITH_D>(acc, m, l, qi, g, bh, a);

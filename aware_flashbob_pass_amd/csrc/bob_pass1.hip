@@ -19,6 +19,8 @@
 // tiles (the whole key range, or one of `nsplit` parts of it). With splits,
 // each wave writes its raw accumulators and row partial sums as a record and
 // a combine kernel sums the records in split order and applies the epilogue.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -309,9 +311,22 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     }
   }
 
-  for (int j = 0; j < nsteps; ++j) {
+  // One pipeline step; S = j % NBUF is a compile-time constant so that every LDS
+  // address is a loop-invariant per-lane offset plus an immediate.
+  auto step = [&](auto S_c, int j) {
+    constexpr int S = decltype(S_c)::value;
+    constexpr int SN = (S + 1) % NBUF, SC = (S + 2) % NBUF;
+    const T* ck = lds + (S * NT + 0) * G::ROW_ELEMS;
+    const T* cv = lds + (S * NT + 1) * G::ROW_ELEMS;
+    const T* cuk = lds + (S * NT + 2) * G::ROW_ELEMS;
+    const T* cuv = lds + (S * NT + 3) * G::ROW_ELEMS;
+    const T* nk = lds + (SN * NT + 0) * G::ROW_ELEMS;
+    const T* nv = lds + (SN * NT + 1) * G::ROW_ELEMS;
+    const T* nuk = lds + (SN * NT + 2) * G::ROW_ELEMS;
+    const T* nuv = lds + (SN * NT + 3) * G::ROW_ELEMS;
     if (j + 2 < nsteps) {
-      T* dst[NT] = {stage(j + 2, 0), stage(j + 2, 1), stage(j + 2, 2), stage(j + 2, 3)};
+      T* dst[NT] = {lds + (SC * NT + 0) * G::ROW_ELEMS, lds + (SC * NT + 1) * G::ROW_ELEMS,
+                    lds + (SC * NT + 2) * G::ROW_ELEMS, lds + (SC * NT + 3) * G::ROW_ELEMS};
       pf.commit(dst, tid);
     }
     if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
@@ -348,32 +363,23 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         vset<TT>(pp[kk], ss, p);
         vset<TT>(pg[kk], ss, vpg);
       };
-      // phase 1: next step's score tiles (matrix cores) with rows 0..7 (vector ALUs)
-      const T* nk = stage(j + 1, 0);
-      const T* nv = stage(j + 1, 1);
-      const T* nuk = stage(j + 1, 2);
-      const T* nuv = stage(j + 1, 3);
+      // phase 1: next step's score tiles (matrix cores) with rows 0..7 (vector ALUs);
+      // the last step also forms "next" tiles from a stale stage, never used
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        if (act_next) {
-          const V ak = lds_row_op<TT, D>(nk, n, t, g);
-          const V av = lds_row_op<TT, D>(nv, n, t, g);
-          const V auk = lds_row_op<TT, D>(nuk, n, t, g);
-          const V auv = lds_row_op<TT, D>(nuv, n, t, g);
-          sx = TT::mfma(ak, bq[t], sx);
-          gx = TT::mfma(ak, buq[t], gx);
-          gx = TT::mfma(auk, bq[t], gx);
-          px = TT::mfma(av, bdo[t], px);
-          hx = TT::mfma(auv, bdo[t], hx);
-        }
+        const V ak = lds_row_op<TT, D>(nk, n, t, g);
+        const V av = lds_row_op<TT, D>(nv, n, t, g);
+        const V auk = lds_row_op<TT, D>(nuk, n, t, g);
+        const V auv = lds_row_op<TT, D>(nuv, n, t, g);
+        sx = TT::mfma(ak, bq[t], sx);
+        gx = TT::mfma(ak, buq[t], gx);
+        gx = TT::mfma(auk, bq[t], gx);
+        px = TT::mfma(av, bdo[t], px);
+        hx = TT::mfma(auv, bdo[t], hx);
 #pragma unroll
         for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
       }
       // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
-      const T* ck = stage(j, 0);
-      const T* cv = stage(j, 1);
-      const T* cuk = stage(j, 2);
-      const T* cuv = stage(j, 3);
 #pragma unroll
       for (int t = 0; t < NK; ++t)
 #pragma unroll
@@ -396,10 +402,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     } else if (act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        const V ak = lds_row_op<TT, D>(stage(j + 1, 0), n, t, g);
-        const V av = lds_row_op<TT, D>(stage(j + 1, 1), n, t, g);
-        const V auk = lds_row_op<TT, D>(stage(j + 1, 2), n, t, g);
-        const V auv = lds_row_op<TT, D>(stage(j + 1, 3), n, t, g);
+        const V ak = lds_row_op<TT, D>(nk, n, t, g);
+        const V av = lds_row_op<TT, D>(nv, n, t, g);
+        const V auk = lds_row_op<TT, D>(nuk, n, t, g);
+        const V auv = lds_row_op<TT, D>(nuv, n, t, g);
         sx = TT::mfma(ak, bq[t], sx);
         gx = TT::mfma(ak, buq[t], gx);
         gx = TT::mfma(auk, bq[t], gx);
@@ -412,7 +418,18 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     pc = px;
     hc = hx;
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int j = 0;
+  for (; j + NBUF <= nsteps; j += NBUF) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
+    step(I2{}, j + 2);
   }
+  if (j < nsteps) step(I0{}, j);
+  if (j + 1 < nsteps) step(I1{}, j + 1);
 
   if (a.nsplit == 1) {
     pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);

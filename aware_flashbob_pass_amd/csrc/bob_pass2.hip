@@ -14,6 +14,8 @@
 // Q, dO, UQ (row-major and transposed copies) and the four row scalars
 // through LDS. With splits of the query range, each wave writes raw
 // accumulators and a reduce kernel sums them in split order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -271,8 +273,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     for (int t = 0; t < DK; ++t) scores_kstep(0, t, sc, gc, pc, hc);
   }
 
-  for (int j = 0; j < nsteps; ++j) {
-    if (j + 2 < nsteps) commit(j + 2);
+  auto step = [&](auto S_c, int j) {
+    constexpr int S = decltype(S_c)::value;
+    constexpr int SN = (S + 1) % NBUF;
+    if (j + 2 < nsteps) commit((S + 2) % NBUF);
     if (j + 3 < nsteps) {
       pf.load(src, (it_begin + j + 3) * kTile, N, tid);
       load_scal((it_begin + j + 3) * kTile);
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     const int i0 = (it_begin + j) * kTile;
     f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
     if (act) {
-      const float* sv = scal(j);
+      const float* sv = scal(S);
       float lqv[16], dqv[16], alv[16], eqv[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
       };
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        if (act_next) scores_kstep(j + 1, t, sx, gx, px, hx);
+        scores_kstep(SN, t, sx, gx, px, hx);  // stale (unused) on the last step
 #pragma unroll
         for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
       }
@@ -329,9 +333,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
       for (int t = 0; t < NK; ++t)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const V tuq = lds_tr_op<TT, D>(tile(j, 2), mb, t, lane);
-          const V tq = lds_tr_op<TT, D>(tile(j, 0), mb, t, lane);
-          const V tdo = lds_tr_op<TT, D>(tile(j, 1), mb, t, lane);
+          const V tuq = lds_tr_op<TT, D>(tile(S, 2), mb, t, lane);
+          const V tq = lds_tr_op<TT, D>(tile(S, 0), mb, t, lane);
+          const V tdo = lds_tr_op<TT, D>(tile(S, 1), mb, t, lane);
           if (t == 0) {
 #pragma unroll
             for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
@@ -342,14 +346,25 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
         }
     } else if (act_next) {
 #pragma unroll
-      for (int t = 0; t < DK; ++t) scores_kstep(j + 1, t, sx, gx, px, hx);
+      for (int t = 0; t < DK; ++t) scores_kstep(SN, t, sx, gx, px, hx);
     }
     sc = sx;
     gc = gx;
     pc = px;
     hc = hx;
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int j = 0;
+  for (; j + NBUF <= nsteps; j += NBUF) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
+    step(I2{}, j + 2);
   }
+  if (j < nsteps) step(I0{}, j);
+  if (j + 1 < nsteps) step(I1{}, j + 1);
 
   if (a.nsplit == 1) {
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);

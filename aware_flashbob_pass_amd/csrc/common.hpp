@@ -80,14 +80,21 @@ __host__ __device__ constexpr int kappa(int r, int g) { return ((r >> 2) << 3) +
 __host__ __device__ constexpr int tpos(int k) { return (((k >> 2) & 1) << 4) + ((k >> 3) << 2) + (k & 3); }
 
 // ---- LDS tile geometry --------------------------------------------------------
-// Row-major copy: 32 rows x D, row stride RS elements. Transposed copy: D rows
-// (head dims) x 32 columns in tpos() order, row stride TS elements. The pads
-// keep 16-byte operand reads of consecutive lanes on distinct LDS banks.
+// Row-major copy: 32 rows x D, row stride RS elements. For 16-bit types the rows
+// are unpadded and the 16-byte chunks of row r are stored XOR-swizzled,
+// chunk c at position c ^ swz(r), with swz(r) = 2 (r mod 4) + (r / 4 mod 2):
+// the 8 lanes of a 16-byte row read (rows m .. m + 7, one chunk) and the 16
+// lanes of a transposing 8-byte read (rows 4k .. 4k + 3, two adjacent chunks)
+// then both fall on 8 distinct 16-byte bank groups. float32 rows are padded
+// by one element instead. Transposed copy (float32 kernels and the first
+// backward): D rows (head dims) x 32 columns in tpos() order, row stride TS.
+__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
 template <class TT, int D>
 struct Geo {
   using T = typename TT::elem;
   static constexpr int PAD = (sizeof(T) == 2) ? 8 : 1;
-  static constexpr int RS = D + PAD;
+  static constexpr int RS = (sizeof(T) == 2) ? D : D + 1;
   static constexpr int TS = kTile + PAD;
   static constexpr int ROW_ELEMS = kTile * RS;
   static constexpr int T_ELEMS = D * TS;
@@ -95,6 +102,17 @@ struct Geo {
   static constexpr int NK = kTile / (2 * TT::KPL);  // k-steps over 32 streamed rows
   static constexpr int MB = D / 32;                 // 32-wide head-dim blocks
 };
+
+// Element offset of (row, col) in a row-major LDS tile (col: 4-element aligned
+// within its 16-byte chunk for 16-bit types).
+template <class TT, int D>
+__device__ inline int roff(int row, int col) {
+  if constexpr (sizeof(typename TT::elem) == 2) {
+    return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+  } else {
+    return row * Geo<TT, D>::RS + col;
+  }
+}
 
 // Stage rows [r0, r0 + 32) of a [N][D] tensor into LDS (row-major copy `rowbuf`
 // and/or transposed copy `tbuf`, either may be null). Rows >= N read as zero.
@@ -117,7 +135,7 @@ __device__ inline void stage_tile(const typename TT::elem* __restrict__ src, int
     const T* v = reinterpret_cast<const T*>(&raw);
     if (rowbuf) {
       if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<uint4*>(rowbuf + row * G::RS + e0) = raw;
+        *reinterpret_cast<uint4*>(rowbuf + roff<TT, D>(row, e0)) = raw;
       } else {
 #pragma unroll
         for (int e = 0; e < CH; ++e) rowbuf[row * G::RS + e0 + e] = v[e];
@@ -134,8 +152,7 @@ __device__ inline void stage_tile(const typename TT::elem* __restrict__ src, int
 // A operand of a score tile: streamed row m = lane % 32, head dims of k-step t.
 template <class TT, int D>
 __device__ inline typename TT::vec lds_row_op(const typename TT::elem* rowbuf, int m, int t, int g) {
-  using G = Geo<TT, D>;
-  const typename TT::elem* p = rowbuf + m * G::RS + t * 2 * TT::KPL + g * TT::KPL;
+  const typename TT::elem* p = rowbuf + roff<TT, D>(m, t * 2 * TT::KPL + g * TT::KPL);
   return *reinterpret_cast<const typename TT::vec*>(p);
 }
 
@@ -195,7 +212,6 @@ struct StagePrefetch {
       }
   }
   __device__ inline void commit(T* const (&dst)[NT], int tid) const {
-    using G = Geo<TT, D>;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -203,7 +219,7 @@ struct StagePrefetch {
         const int c = tid + p * NTHREADS;
         if (c < NCH) {
           const int row = c / CPR, e0 = (c % CPR) * CH;
-          *reinterpret_cast<uint4*>(dst[t] + row * G::RS + e0) = r[t][p];
+          *reinterpret_cast<uint4*>(dst[t] + roff<TT, D>(row, e0)) = r[t][p];
         }
       }
   }
@@ -223,13 +239,12 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 // the same rows the score-tile B operand holds in its slots.
 template <class TT, int D>
 __device__ inline typename TT::vec lds_tr_op(const typename TT::elem* rowbuf, int mb, int t, int lane) {
-  using G = Geo<TT, D>;
   static_assert(TT::KPL == 8, "transposing LDS loads are for 16-bit types");
   const int i = lane & 15, g = lane >> 5, half = (lane >> 4) & 1;
   const int col = mb * 32 + half * 16 + (i & 3) * 4;
   const int row0 = t * 16 + g * 4 + (i >> 2);
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + row0 * G::RS + col));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + (row0 + 8) * G::RS + col));
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + roff<TT, D>(row0, col)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(rowbuf + roff<TT, D>(row0 + 8, col)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename TT::vec, v);
