@@ -45,19 +45,22 @@ constexpr int kMaxSplits = 64;
 constexpr int kTargetBlocks = 256;   // one workgroup per compute unit
 constexpr int kMinTilesPerSplit = 4; // 4 x 32 streamed rows per split at least
 
-int auto_splits(int BH, int N) {
+int auto_splits(int BH, int N, int target = kTargetBlocks) {
   const long long blocks = (long long)fb::row_tiles(N) * BH;
-  if (blocks >= kTargetBlocks) return 1;
+  if (blocks >= target) return 1;
   const int steps = (N + 31) / 32;
-  int s = (int)((kTargetBlocks + blocks - 1) / blocks);
+  int s = (int)((target + blocks - 1) / blocks);
   s = std::min(s, std::max(1, steps / kMinTilesPerSplit));
   return std::max(1, std::min(s, kMaxSplits));
 }
 
-void splits_for(int BH, int N, int* s1, int* s2) {
+// The statistics kernel fits two workgroups per compute unit, so by default it
+// splits to fill 512; with an explicit pass-1 split it follows that value.
+void splits_for(int BH, int N, int* s0, int* s1, int* s2) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   *s1 = g_split1 > 0 ? g_split1 : auto_splits(BH, N);
   *s2 = g_split2 > 0 ? g_split2 : auto_splits(BH, N);
+  *s0 = g_split1 > 0 ? g_split1 : auto_splits(BH, N, 2 * kTargetBlocks);
 }
 
 // ---- kernel timing ------------------------------------------------------------
@@ -137,8 +140,8 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   WsLayout w{};
   const size_t BH = (size_t)B * H;
   const size_t vec = align256(BH * N * sizeof(float));
-  splits_for((int)BH, N, &w.s1, &w.s2);
-  w.s0 = dtype == FB_F32 ? 1 : w.s1;  // the float32 statistics kernel does not split
+  splits_for((int)BH, N, &w.s0, &w.s1, &w.s2);
+  if (dtype == FB_F32) w.s0 = 1;  // the float32 statistics kernel does not split
   size_t off = 0;
   w.o = off;
   off += align256(BH * N * d * esize(dtype));

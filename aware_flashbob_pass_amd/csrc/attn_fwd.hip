@@ -184,9 +184,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + blockIdx.x) * 4 + wave;
   float* R = a.part + rec * fwd_record_floats(D);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) R[(mb * 16 + r) * 64 + lane] = acc[mb][r];
+  for (int mb = 0; mb < MB; ++mb) store_acc16(R + (mb * 64 + lane) * 16, acc[mb]);  // [MB][64 lanes][16]
   R[MB * 16 * 64 + lane] = m;
   R[MB * 16 * 64 + 64 + lane] = l;
 }
@@ -214,9 +212,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
     const float w = fast_exp2(R[MB * 16 * 64 + lane] - M);
     l += w * R[MB * 16 * 64 + 64 + lane];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][r] += w * R[(mb * 16 + r) * 64 + lane];
+    for (int mb = 0; mb < MB; ++mb) acc[mb] += w * load_acc16(R + (mb * 64 + lane) * 16);
   }
   fwd_epilogue<TT, D, WITH_D>(acc, M, l, qi, g, bh, a);
 }

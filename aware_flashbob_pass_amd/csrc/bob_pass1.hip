@@ -31,7 +31,7 @@ struct P1 {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   static constexpr int MB = G::MB;
-  // record layout (floats): acc[4][MB][16][64 lanes], alpha_p[64], e0_p[64]
+  // record layout (floats): acc[4][MB][64 lanes][16], alpha_p[64], e0_p[64]
   static constexpr int ACC_FLOATS = 4 * MB * 16 * 64;
 };
 
@@ -87,14 +87,12 @@ __device__ inline void pass1_write_record(const f32x16 (&A)[Geo<TT, D>::MB], con
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
   float* R = a.part + rec * pass1_record_floats(D);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      R[((0 * MB + mb) * 16 + r) * 64 + lane] = A[mb][r];
-      R[((1 * MB + mb) * 16 + r) * 64 + lane] = B[mb][r];
-      R[((2 * MB + mb) * 16 + r) * 64 + lane] = C[mb][r];
-      R[((3 * MB + mb) * 16 + r) * 64 + lane] = X[mb][r];
-    }
+  for (int mb = 0; mb < MB; ++mb) {
+    store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);
+    store_acc16(R + ((1 * MB + mb) * 64 + lane) * 16, B[mb]);
+    store_acc16(R + ((2 * MB + mb) * 64 + lane) * 16, C[mb]);
+    store_acc16(R + ((3 * MB + mb) * 64 + lane) * 16, X[mb]);
+  }
   R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
   R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;
 }
@@ -461,14 +459,12 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
     const size_t rec = (((size_t)sp * a.BH + bh) * qt_count + blockIdx.x) * 4 + wave;
     const float* R = a.part + rec * pass1_record_floats(D);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        A[mb][r] += R[((0 * MB + mb) * 16 + r) * 64 + lane];
-        B[mb][r] += R[((1 * MB + mb) * 16 + r) * 64 + lane];
-        C[mb][r] += R[((2 * MB + mb) * 16 + r) * 64 + lane];
-        X[mb][r] += R[((3 * MB + mb) * 16 + r) * 64 + lane];
-      }
+    for (int mb = 0; mb < MB; ++mb) {
+      A[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+      B[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+      C[mb] += load_acc16(R + ((2 * MB + mb) * 64 + lane) * 16);
+      X[mb] += load_acc16(R + ((3 * MB + mb) * 64 + lane) * 16);
+    }
     alpha_p += R[P1<TT, D>::ACC_FLOATS + lane];
     e0_p += R[P1<TT, D>::ACC_FLOATS + 64 + lane];
   }

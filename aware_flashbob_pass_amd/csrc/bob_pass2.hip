@@ -47,14 +47,12 @@ __device__ inline void pass2_write_record(const f32x16 (&dK)[Geo<TT, D>::MB], co
                                           int split, int bh, int wave, int lane, const Pass2Args& a) {
   constexpr int MB = Geo<TT, D>::MB;
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
-  float* R = a.part + rec * pass2_record_floats(D);
+  float* R = a.part + rec * pass2_record_floats(D);  // [2][MB][64 lanes][16]
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      R[((0 * MB + mb) * 16 + r) * 64 + lane] = dK[mb][r];
-      R[((1 * MB + mb) * 16 + r) * 64 + lane] = dV[mb][r];
-    }
+  for (int mb = 0; mb < MB; ++mb) {
+    store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, dK[mb]);
+    store_acc16(R + ((1 * MB + mb) * 64 + lane) * 16, dV[mb]);
+  }
 }
 
 // Single-buffered variant (transposed LDS copies); used for float32 inputs.
@@ -392,12 +390,10 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
     const size_t rec = (((size_t)sp * a.BH + bh) * kt_count + blockIdx.x) * 4 + wave;
     const float* R = a.part + rec * pass2_record_floats(D);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dK[mb][r] += R[((0 * MB + mb) * 16 + r) * 64 + lane];
-        dV[mb][r] += R[((1 * MB + mb) * 16 + r) * 64 + lane];
-      }
+    for (int mb = 0; mb < MB; ++mb) {
+      dK[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+      dV[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+    }
   }
   pass2_epilogue<TT, D>(dK, dV, kj, g, bh, a);
 }

@@ -81,14 +81,21 @@ __host__ __device__ constexpr int tpos(int k) { return (((k >> 2) & 1) << 4) + (
 
 // ---- LDS tile geometry --------------------------------------------------------
 // Row-major copy: 32 rows x D, row stride RS elements. For 16-bit types the rows
-// are unpadded and the 16-byte chunks of row r are stored XOR-swizzled,
-// chunk c at position c ^ swz(r), with swz(r) = 2 (r mod 4) + (r / 4 mod 2):
-// the 8 lanes of a 16-byte row read (rows m .. m + 7, one chunk) and the 16
-// lanes of a transposing 8-byte read (rows 4k .. 4k + 3, two adjacent chunks)
-// then both fall on 8 distinct 16-byte bank groups. float32 rows are padded
-// by one element instead. Transposed copy (float32 kernels and the first
-// backward): D rows (head dims) x 32 columns in tpos() order, row stride TS.
-__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// are unpadded and the 16-byte chunks of row r are stored XOR-swizzled: chunk c
+// at position c ^ swz(r). Measured on the MI355X with an LDS read microbenchmark
+// (16 lanes of a 16-byte read are served per cycle from 64 four-byte banks), the
+// swizzle (r / 2) mod 8 for 128-byte rows (d = 64) is as fast as a contiguous
+// read for the 16-byte row reads of the score operands and the fastest of the
+// layouts tried for the transposing 8-byte reads. 256-byte rows (d = 128) use
+// r mod 16 so that 16 consecutive rows read at one chunk hit 16 distinct
+// 16-byte bank groups. float32 rows are padded by one element instead.
+// Transposed copy (float32 kernels and the first backward): D rows (head dims)
+// x 32 columns in tpos() order, row stride TS.
+template <int D>
+__device__ inline int swz(int row) {
+  if constexpr (D == 64) return (row >> 1) & 7;
+  return row & 15;
+}
 
 template <class TT, int D>
 struct Geo {
@@ -108,7 +115,7 @@ struct Geo {
 template <class TT, int D>
 __device__ inline int roff(int row, int col) {
   if constexpr (sizeof(typename TT::elem) == 2) {
-    return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+    return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
   } else {
     return row * Geo<TT, D>::RS + col;
   }
@@ -255,6 +262,25 @@ __device__ inline f32x16 zero16() {
 #pragma unroll
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   return z;
+}
+
+// One lane's 16 accumulator values as 4 x 16-byte global accesses.
+__device__ inline void store_acc16(float* dst, const f32x16& v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    reinterpret_cast<f32x4*>(dst)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+__device__ inline f32x16 load_acc16(const float* src) {
+  f32x16 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(src)[q];
+    v[4 * q] = x[0];
+    v[4 * q + 1] = x[1];
+    v[4 * q + 2] = x[2];
+    v[4 * q + 3] = x[3];
+  }
+  return v;
 }
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
