@@ -227,6 +227,34 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
   pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, a);
 }
 
+// Interleaving request for one pipelined pass-1 step (one basic block): each
+// matrix-core op is followed by a share of the element-wise vector work and by
+// the LDS reads of the NEXT k-step (operands are fetched one k-step ahead).
+// Masks: 0x008 matrix core, 0x002 vector ALU, 0x100 LDS read.
+template <int DK, int MB>
+__device__ inline void pass1_schedule() {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // k-step 0 operands
+#pragma unroll
+  for (int i = 0; i < 5 * DK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 6 * MB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 6 * MB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
 // Pipelined variant for 16-bit inputs. LDS holds three stages of row-major
 // K, V, UK, UV tiles (32 keys each); the registers of every thread prefetch the
 // stage two steps ahead, so each step has a single barrier and no exposed
@@ -362,41 +390,55 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         vset<TT>(pg[kk], ss, vpg);
       };
       // phase 1: next step's score tiles (matrix cores) with rows 0..7 (vector ALUs);
-      // the last step also forms "next" tiles from a stale stage, never used
+      // the last step also forms "next" tiles from a stale stage, never used.
+      // LDS operands are fetched one k-step ahead of the matrix-core ops using them.
+      V ro[2][4];
+      auto fetch_row = [&](int t, V (&o)[4]) {
+        o[0] = lds_row_op<TT, D>(nk, n, t, g);
+        o[1] = lds_row_op<TT, D>(nv, n, t, g);
+        o[2] = lds_row_op<TT, D>(nuk, n, t, g);
+        o[3] = lds_row_op<TT, D>(nuv, n, t, g);
+      };
+      fetch_row(0, ro[0]);
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        const V ak = lds_row_op<TT, D>(nk, n, t, g);
-        const V av = lds_row_op<TT, D>(nv, n, t, g);
-        const V auk = lds_row_op<TT, D>(nuk, n, t, g);
-        const V auv = lds_row_op<TT, D>(nuv, n, t, g);
-        sx = TT::mfma(ak, bq[t], sx);
-        gx = TT::mfma(ak, buq[t], gx);
-        gx = TT::mfma(auk, bq[t], gx);
-        px = TT::mfma(av, bdo[t], px);
-        hx = TT::mfma(auv, bdo[t], hx);
+        if (t + 1 < DK) fetch_row(t + 1, ro[(t + 1) & 1]);
+        const V(&o)[4] = ro[t & 1];
+        sx = TT::mfma(o[0], bq[t], sx);
+        gx = TT::mfma(o[0], buq[t], gx);
+        px = TT::mfma(o[1], bdo[t], px);
+        gx = TT::mfma(o[2], bq[t], gx);
+        hx = TT::mfma(o[3], bdo[t], hx);
 #pragma unroll
         for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
       }
       // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
+      V to[2][4];
+      auto fetch_tr = [&](int q, V (&o)[4]) {
+        const int t = q / MB, mb = q % MB;
+        o[0] = lds_tr_op<TT, D>(ck, mb, t, lane);
+        o[1] = lds_tr_op<TT, D>(cuk, mb, t, lane);
+        o[2] = lds_tr_op<TT, D>(cv, mb, t, lane);
+        o[3] = lds_tr_op<TT, D>(cuv, mb, t, lane);
+      };
+      fetch_tr(0, to[0]);
 #pragma unroll
-      for (int t = 0; t < NK; ++t)
+      for (int q = 0; q < NK * MB; ++q) {
+        const int t = q / MB, mb = q % MB;
+        if (q + 1 < NK * MB) fetch_tr(q + 1, to[(q + 1) & 1]);
+        if (t == 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const V tk = lds_tr_op<TT, D>(ck, mb, t, lane);
-          const V tuk = lds_tr_op<TT, D>(cuk, mb, t, lane);
-          const V tv = lds_tr_op<TT, D>(cv, mb, t, lane);
-          const V tuv = lds_tr_op<TT, D>(cuv, mb, t, lane);
-          if (t == 0) {
-#pragma unroll
-            for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
-          }
-          accA[mb] = TT::mfma(tuk, wa[t], accA[mb]);
-          accA[mb] = TT::mfma(tk, wb[t], accA[mb]);
-          accB[mb] = TT::mfma(tk, pd[t], accB[mb]);
-          accC[mb] = TT::mfma(tk, pp[t], accC[mb]);
-          accX[mb] = TT::mfma(tuv, pp[t], accX[mb]);
-          accX[mb] = TT::mfma(tv, pg[t], accX[mb]);
+          for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
         }
+        const V(&o)[4] = to[q & 1];
+        accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);
+        accB[mb] = TT::mfma(o[0], pd[t], accB[mb]);
+        accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);
+        accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);
+        accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);
+        accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);
+      }
+      pass1_schedule<DK, MB>();
     } else if (act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
