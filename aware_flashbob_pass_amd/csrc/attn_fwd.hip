@@ -95,13 +95,14 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
   auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
 
-  StagePrefetch<TT, D, NT, kBlock> pf;
-  for (int j = 0; j < 2 && j < nsteps; ++j) {
-    pf.load(src, (kt_begin + j) * kTile, N, tid);
-    T* dst[NT] = {stage(j, 0), stage(j, 1)};
-    pf.commit(dst, tid);
-  }
-  if (nsteps > 2) pf.load(src, (kt_begin + 2) * kTile, N, tid);
+  auto issue = [&](int stg, int j) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS, wave,
+                                        lane);
+  };
+  for (int j = 0; j < 2 && j < nsteps; ++j) issue(j, j);
+  wait_vmem();
   __syncthreads();
 
   f32x16 sc = zero16();
@@ -112,11 +113,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
     constexpr int SN = (S + 1) % NBUF, SC = (S + 2) % NBUF;
-    if (j + 2 < nsteps) {
-      T* dst[NT] = {stage(SC, 0), stage(SC, 1)};
-      pf.commit(dst, tid);
-    }
-    if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
+    if (j + 2 < nsteps) issue(SC, j + 2);  // buffer SC was last read in step j - 1
     const bool act = active(j);
     const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int k0 = (kt_begin + j) * kTile;
@@ -163,6 +160,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
       for (int t = 0; t < DK; ++t) sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);
     }
     sc = sx;
+    wait_vmem();
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;

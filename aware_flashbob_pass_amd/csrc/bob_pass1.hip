@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   using V = typename TT::vec;
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
   constexpr int NT = 4, NBUF = 3;
+  // d = 64 keeps the next step's score tiles in registers (software pipelining);
+  // d = 128 has no room for them next to 256 accumulator registers and forms
+  // each step's score tiles at the start of the step instead.
+  constexpr bool PIPE = D == 64;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
@@ -311,18 +315,19 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
   auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
 
-  StagePrefetch<TT, D, NT, kBlock> pf;
-  for (int j = 0; j < 2 && j < nsteps; ++j) {
-    pf.load(src, (kt_begin + j) * kTile, N, tid);
-    T* dst[NT] = {stage(j, 0), stage(j, 1), stage(j, 2), stage(j, 3)};
-    pf.commit(dst, tid);
-  }
-  if (nsteps > 2) pf.load(src, (kt_begin + 2) * kTile, N, tid);
+  auto issue = [&](int stg, int j) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS, wave,
+                                        lane);
+  };
+  for (int j = 0; j < 2 && j < nsteps; ++j) issue(j, j);
+  wait_vmem();
   __syncthreads();
 
   // score tiles of the current step (c) and of the next step (x)
   f32x16 sc = zero16(), gc = zero16(), pc = zero16(), hc = zero16();
-  if (nsteps > 0 && active(0)) {
+  if (PIPE && nsteps > 0 && active(0)) {
 #pragma unroll
     for (int t = 0; t < DK; ++t) {
       const V ak = lds_row_op<TT, D>(stage(0, 0), n, t, g);
@@ -350,18 +355,31 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     const T* nv = lds + (SN * NT + 1) * G::ROW_ELEMS;
     const T* nuk = lds + (SN * NT + 2) * G::ROW_ELEMS;
     const T* nuv = lds + (SN * NT + 3) * G::ROW_ELEMS;
-    if (j + 2 < nsteps) {
-      T* dst[NT] = {lds + (SC * NT + 0) * G::ROW_ELEMS, lds + (SC * NT + 1) * G::ROW_ELEMS,
-                    lds + (SC * NT + 2) * G::ROW_ELEMS, lds + (SC * NT + 3) * G::ROW_ELEMS};
-      pf.commit(dst, tid);
-    }
-    if (j + 3 < nsteps) pf.load(src, (kt_begin + j + 3) * kTile, N, tid);
+    if (j + 2 < nsteps) issue(SC, j + 2);  // buffer SC was last read in step j - 1
     const bool act = active(j);
     const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int k0 = (kt_begin + j) * kTile;
     f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
 
     if (act) {
+      if constexpr (!PIPE) {
+        sc = zero16();
+        gc = zero16();
+        pc = zero16();
+        hc = zero16();
+#pragma unroll
+        for (int t = 0; t < DK; ++t) {
+          const V ak = lds_row_op<TT, D>(ck, n, t, g);
+          const V av = lds_row_op<TT, D>(cv, n, t, g);
+          const V auk = lds_row_op<TT, D>(cuk, n, t, g);
+          const V auv = lds_row_op<TT, D>(cuv, n, t, g);
+          sc = TT::mfma(ak, bq[t], sc);
+          gc = TT::mfma(ak, buq[t], gc);
+          gc = TT::mfma(auk, bq[t], gc);
+          pc = TT::mfma(av, bdo[t], pc);
+          hc = TT::mfma(auv, bdo[t], hc);
+        }
+      }
       // log2-domain scores, masked where the key is out of range or after the query
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = sc[r] * cs - lq;
@@ -399,18 +417,23 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         o[2] = lds_row_op<TT, D>(nuk, n, t, g);
         o[3] = lds_row_op<TT, D>(nuv, n, t, g);
       };
-      fetch_row(0, ro[0]);
+      if constexpr (PIPE) {
+        fetch_row(0, ro[0]);
 #pragma unroll
-      for (int t = 0; t < DK; ++t) {
-        if (t + 1 < DK) fetch_row(t + 1, ro[(t + 1) & 1]);
-        const V(&o)[4] = ro[t & 1];
-        sx = TT::mfma(o[0], bq[t], sx);
-        gx = TT::mfma(o[0], buq[t], gx);
-        px = TT::mfma(o[1], bdo[t], px);
-        gx = TT::mfma(o[2], bq[t], gx);
-        hx = TT::mfma(o[3], bdo[t], hx);
+        for (int t = 0; t < DK; ++t) {
+          if (t + 1 < DK) fetch_row(t + 1, ro[(t + 1) & 1]);
+          const V(&o)[4] = ro[t & 1];
+          sx = TT::mfma(o[0], bq[t], sx);
+          gx = TT::mfma(o[0], buq[t], gx);
+          px = TT::mfma(o[1], bdo[t], px);
+          gx = TT::mfma(o[2], bq[t], gx);
+          hx = TT::mfma(o[3], bdo[t], hx);
 #pragma unroll
-        for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
+          for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) elementwise(r);
       }
       // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
       V to[2][4];
@@ -438,8 +461,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);
         accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);
       }
-      pass1_schedule<DK, MB>();
-    } else if (act_next) {
+      if constexpr (PIPE) pass1_schedule<DK, MB>();
+    } else if (PIPE && act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
         const V ak = lds_row_op<TT, D>(nk, n, t, g);
@@ -453,10 +476,13 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         hx = TT::mfma(auv, bdo[t], hx);
       }
     }
-    sc = sx;
-    gc = gx;
-    pc = px;
-    hc = hx;
+    if constexpr (PIPE) {
+      sc = sx;
+      gc = gx;
+      pc = px;
+      hc = hx;
+    }
+    wait_vmem();
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;

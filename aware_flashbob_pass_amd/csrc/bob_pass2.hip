@@ -230,8 +230,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   auto scal = [&](int j) { return reinterpret_cast<float*>(lds + (j % NBUF) * STAGE_ELEMS + NT * G::ROW_ELEMS); };
   auto active = [&](int j) { return !CAUSAL || (it_begin + j) * kTile + kTile - 1 >= k0w; };
 
-  StagePrefetch<TT, D, NT, kBlock> pf;
-  float sreg = 0.f;  // one of the 4 x 32 row scalars of the prefetched stage (threads 0..127)
+  float sreg = 0.f;  // one of the 4 x 32 row scalars of a later stage (threads 0..127)
   auto load_scal = [&](int i0) {
     sreg = 0.f;
     if (tid < 4 * kTile) {
@@ -239,20 +238,21 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
       if (row < N) sreg = vsrc[which][row] * (which == 0 ? kLog2e : 1.f);
     }
   };
-  auto commit = [&](int j) {
-    T* dst[NT] = {tile(j, 0), tile(j, 1), tile(j, 2)};
-    pf.commit(dst, tid);
-    if (tid < 4 * kTile) scal(j)[tid] = sreg;
+  auto put_scal = [&](int stg) {
+    if (tid < 4 * kTile) scal(stg)[tid] = sreg;
+  };
+  auto issue = [&](int stg, int j) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      stage_direct<TT, D, kBlock / 64>(src[t], (it_begin + j) * kTile, N, tile(stg, t), wave, lane);
   };
   for (int j = 0; j < 2 && j < nsteps; ++j) {
-    pf.load(src, (it_begin + j) * kTile, N, tid);
+    issue(j, j);
     load_scal((it_begin + j) * kTile);
-    commit(j);
+    put_scal(j);
   }
-  if (nsteps > 2) {
-    pf.load(src, (it_begin + 2) * kTile, N, tid);
-    load_scal((it_begin + 2) * kTile);
-  }
+  if (nsteps > 2) load_scal((it_begin + 2) * kTile);
+  wait_vmem();
   __syncthreads();
 
   f32x16 sc = zero16(), gc = zero16(), pc = zero16(), hc = zero16();
@@ -274,11 +274,11 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
     constexpr int SN = (S + 1) % NBUF;
-    if (j + 2 < nsteps) commit((S + 2) % NBUF);
-    if (j + 3 < nsteps) {
-      pf.load(src, (it_begin + j + 3) * kTile, N, tid);
-      load_scal((it_begin + j + 3) * kTile);
+    if (j + 2 < nsteps) {  // buffer (S + 2) % NBUF was last read in step j - 1
+      issue((S + 2) % NBUF, j + 2);
+      put_scal((S + 2) % NBUF);
     }
+    if (j + 3 < nsteps) load_scal((it_begin + j + 3) * kTile);
     const bool act = active(j);
     const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int i0 = (it_begin + j) * kTile;
@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     gc = gx;
     pc = px;
     hc = hx;
+    wait_vmem();
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;

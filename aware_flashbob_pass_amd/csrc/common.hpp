@@ -232,6 +232,35 @@ struct StagePrefetch {
   }
 };
 
+// Direct global -> LDS staging of one 32-row stage of a [N][D] tensor (16-bit
+// types): each wave issues global_load_lds_dwordx4, whose lane L writes the 16
+// bytes at (wave-uniform LDS base) + 16 L. LDS slot s of the tile is row
+// s / (D / 8), physical chunk s % (D / 8); its source is the logical chunk
+// (physical chunk ^ swz(row)) of that row, which realises the XOR swizzle of
+// roff(). Rows >= N fetch row N - 1 (finite values; every consumer masks them
+// out). Completion: s_waitcnt vmcnt(0) then a workgroup barrier.
+template <class TT, int D, int NWAVES>
+__device__ inline void stage_direct(const typename TT::elem* __restrict__ src, int r0, int N,
+                                    typename TT::elem* tile, int wave, int lane) {
+  static_assert(sizeof(typename TT::elem) == 2, "16-bit types only");
+  constexpr int SPR = D / 8;                     // 16-byte slots per row
+  constexpr int PER_WAVE = kTile * SPR / (64 * NWAVES);
+  static_assert(PER_WAVE * 64 * NWAVES == kTile * SPR, "stage must split evenly over the waves");
+#pragma unroll
+  for (int p = 0; p < PER_WAVE; ++p) {
+    const int blk = p * NWAVES + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / SPR, pc = slot % SPR;
+    const int c = pc ^ swz<D>(row);
+    const int grow = min(r0 + row, N - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (size_t)grow * D + c * 8),
+                                     (__attribute__((address_space(3))) void*)(tile + blk * 64 * 8),
+                                     16, 0, 0);
+  }
+}
+
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
