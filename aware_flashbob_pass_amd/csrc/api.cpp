@@ -128,6 +128,8 @@ fb_status_t hip_fail(hipError_t e, const char* what) {
   return fail(FB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+DT to_dt(fb_dtype_t t) { return t == FB_BF16 ? DT::BF16 : (t == FB_F16 ? DT::F16 : DT::F32); }
+
 // ---- workspace layout ------------------------------------------------------------
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -154,7 +156,8 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   w.e = off;
   off += vec;
   const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
-  const size_t p1 = w.s1 > 1 ? (size_t)w.s1 * tiles * fb::pass1_record_floats(d) * sizeof(float) : 0;
+  const int nh = fb::pass1_halves(to_dt(dtype), d);
+  const size_t p1 = w.s1 > 1 ? (size_t)w.s1 * tiles * nh * fb::pass1_record_floats(d / nh) * sizeof(float) : 0;
   const size_t p2 = w.s2 > 1 ? (size_t)w.s2 * tiles * fb::pass2_record_floats(d) * sizeof(float) : 0;
   const size_t p0 = w.s0 > 1 ? (size_t)w.s0 * tiles * fb::fwd_record_floats(d) * sizeof(float) : 0;
   w.part = off;  // each kernel's records are consumed before the next kernel writes its own
@@ -162,8 +165,6 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   w.total = off;
   return w;
 }
-
-DT to_dt(fb_dtype_t t) { return t == FB_BF16 ? DT::BF16 : (t == FB_F16 ? DT::F16 : DT::F32); }
 
 template <class F>
 fb_status_t run(const char* name, hipStream_t s, F&& launch) {

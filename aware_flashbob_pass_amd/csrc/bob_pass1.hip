@@ -30,19 +30,23 @@ template <class TT, int D>
 struct P1 {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
-  static constexpr int MB = G::MB;
-  // record layout (floats): acc[4][MB][64 lanes][16], alpha_p[64], e0_p[64]
-  static constexpr int ACC_FLOATS = 4 * MB * 16 * 64;
+  // 16-bit d = 128: each workgroup accumulates one half of the head dimension
+  // (the grid's z axis holds split x half); everything else accumulates all of it.
+  static constexpr int NH = (TT::KPL == 8 && D == 128) ? 2 : 1;
+  static constexpr int MBA = G::MB / NH;  // accumulated 32-wide head-dim blocks
+  // record layout (floats): acc[4][MBA][64 lanes][16], alpha_p[64], e0_p[64]
+  static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
 };
 
-// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave.
+// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave (head-dim
+// blocks half * MBA .. half * MBA + MBA - 1).
 template <class TT, int D>
-__device__ inline void pass1_epilogue(const f32x16 (&A)[Geo<TT, D>::MB], const f32x16 (&B)[Geo<TT, D>::MB],
-                                      const f32x16 (&C)[Geo<TT, D>::MB], const f32x16 (&X)[Geo<TT, D>::MB],
-                                      float alpha_p, float e0_p, int qi, int g, int bh,
+__device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
+                                      const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
+                                      float alpha_p, float e0_p, int qi, int g, int bh, int half,
                                       const Pass1Args& a) {
-  using G = Geo<TT, D>;
   using T = typename TT::elem;
+  constexpr int MBA = P1<TT, D>::MBA;
   const int N = a.N;
   const float alpha = alpha_p + xor32(alpha_p);
   const float e0 = e0_p + xor32(e0_p);
@@ -55,37 +59,42 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[Geo<TT, D>::MB], const f
   T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
   const float tau = a.tau;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+  for (int mbl = 0; mbl < MBA; ++mbl)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int dim = mb * 32 + kappa(r4 * 4, g);
+      const int dim = (half * MBA + mbl) * 32 + kappa(r4 * 4, g);
       float o[4], q[4], x[4];
       load4<TT>(O + dim, o);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r4 * 4 + e;
-        q[e] = tau * (A[mb][r] - alpha * B[mb][r] - E * C[mb][r]);
-        x[e] = X[mb][r] - alpha * o[e];
+        q[e] = tau * (A[mbl][r] - alpha * B[mbl][r] - E * C[mbl][r]);
+        x[e] = X[mbl][r] - alpha * o[e];
       }
       store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
       store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
     }
-  if (g == 0) {
+  if (g == 0 && half == 0) {
     a.alpha[row] = alpha;
     a.E[row] = E;
   }
 }
 
-
-// Raw accumulators and row partials of one wave for split `split`.
+// Raw accumulators and row partials of one wave for split `split`, half `half`.
 template <class TT, int D>
-__device__ inline void pass1_write_record(const f32x16 (&A)[Geo<TT, D>::MB], const f32x16 (&B)[Geo<TT, D>::MB],
-                                          const f32x16 (&C)[Geo<TT, D>::MB], const f32x16 (&X)[Geo<TT, D>::MB],
-                                          float alpha_p, float e0_p, int split, int bh, int wave, int lane,
+__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int wave, int half) {
+  constexpr int NH = P1<TT, D>::NH;
+  const size_t rec = ((((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave) * NH + half;
+  return a.part + rec * pass1_record_floats(D / NH);
+}
+
+template <class TT, int D>
+__device__ inline void pass1_write_record(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
+                                          const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
+                                          float alpha_p, float e0_p, int split, int bh, int wave, int lane, int half,
                                           const Pass1Args& a) {
-  constexpr int MB = Geo<TT, D>::MB;
-  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
-  float* R = a.part + rec * pass1_record_floats(D);
+  constexpr int MB = P1<TT, D>::MBA;
+  float* R = pass1_record<TT, D>(a, split, bh, wave, half);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);
@@ -221,10 +230,10 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
   }
 
   if (a.nsplit == 1) {
-    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
+    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, 0, a);
     return;
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, a);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, 0, a);
 }
 
 // Interleaving request for one pipelined pass-1 step (one basic block): each
@@ -273,13 +282,14 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   // d = 128 has no room for them next to 256 accumulator registers and forms
   // each step's score tiles at the start of the step instead.
   constexpr bool PIPE = D == 64;
+  constexpr int NH = P1<TT, D>::NH, MBA = P1<TT, D>::MBA;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  const int N = a.N, bh = blockIdx.y, split = blockIdx.z / NH, half = blockIdx.z % NH;
   const size_t base = (size_t)bh * N * D;
   const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base,
                       reinterpret_cast<const T*>(a.UK) + base, reinterpret_cast<const T*>(a.UV) + base};
@@ -296,9 +306,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   const float cs = a.tau * kLog2e;
   const float tau = a.tau;
 
-  f32x16 accA[MB], accB[MB], accC[MB], accX[MB];
+  f32x16 accA[MBA], accB[MBA], accC[MBA], accX[MBA];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+  for (int mb = 0; mb < MBA; ++mb) {
     accA[mb] = zero16();
     accB[mb] = zero16();
     accC[mb] = zero16();
@@ -438,20 +448,25 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
       // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
       V to[2][4];
       auto fetch_tr = [&](int q, V (&o)[4]) {
-        const int t = q / MB, mb = q % MB;
+        const int t = q / MBA, mb = half * MBA + q % MBA;
         o[0] = lds_tr_op<TT, D>(ck, mb, t, lane);
         o[1] = lds_tr_op<TT, D>(cuk, mb, t, lane);
         o[2] = lds_tr_op<TT, D>(cv, mb, t, lane);
         o[3] = lds_tr_op<TT, D>(cuv, mb, t, lane);
       };
-      fetch_tr(0, to[0]);
+      if constexpr (PIPE) fetch_tr(0, to[0]);
 #pragma unroll
-      for (int q = 0; q < NK * MB; ++q) {
-        const int t = q / MB, mb = q % MB;
-        if (q + 1 < NK * MB) fetch_tr(q + 1, to[(q + 1) & 1]);
+      for (int q = 0; q < NK * MBA; ++q) {
+        const int t = q / MBA, mb = q % MBA;  // mb: accumulator block of this half
+        // d = 128 fetches each k-step's operands just before use (register budget)
+        if constexpr (PIPE) {
+          if (q + 1 < NK * MBA) fetch_tr(q + 1, to[(q + 1) & 1]);
+        } else {
+          fetch_tr(q, to[q & 1]);
+        }
         if (t == 0) {
 #pragma unroll
-          for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
+          for (int r = 8 + mb * 8 / MBA; r < 8 + (mb + 1) * 8 / MBA; ++r) elementwise(r);
         }
         const V(&o)[4] = to[q & 1];
         accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);
@@ -461,7 +476,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);
         accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);
       }
-      if constexpr (PIPE) pass1_schedule<DK, MB>();
+      if constexpr (PIPE) pass1_schedule<DK, MBA>();
     } else if (PIPE && act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
@@ -498,22 +513,20 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   if (j + 1 < nsteps) step(I1{}, j + 1);
 
   if (a.nsplit == 1) {
-    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
+    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, half, a);
     return;
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, a);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, half, a);
 }
 
 // Sum the split records of each wave in split order, then apply the epilogue.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) {
-  using G = Geo<TT, D>;
-  constexpr int MB = G::MB;
+  constexpr int MB = P1<TT, D>::MBA;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y;
+  const int N = a.N, bh = blockIdx.y, half = blockIdx.z;
   const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
-  const int qt_count = row_tiles(N);
   f32x16 A[MB], B[MB], C[MB], X[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -524,8 +537,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
   }
   float alpha_p = 0.f, e0_p = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) {
-    const size_t rec = (((size_t)sp * a.BH + bh) * qt_count + blockIdx.x) * 4 + wave;
-    const float* R = a.part + rec * pass1_record_floats(D);
+    const float* R = pass1_record<TT, D>(a, sp, bh, wave, half);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       A[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
@@ -536,7 +548,8 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
     alpha_p += R[P1<TT, D>::ACC_FLOATS + lane];
     e0_p += R[P1<TT, D>::ACC_FLOATS + 64 + lane];
   }
-  pass1_epilogue<TT, D>(A, B, C, X, alpha_p, e0_p, qi, g, bh, a);
+  (void)N;
+  pass1_epilogue<TT, D>(A, B, C, X, alpha_p, e0_p, qi, g, bh, half, a);
 }
 
 template <class TT, int D>
@@ -549,7 +562,7 @@ static size_t pass1_lds_bytes() {
 template <class TT, int D, bool CAUSAL>
 static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
   const size_t lds = pass1_lds_bytes<TT, D>();
-  dim3 grid(row_tiles(a.N), a.BH, a.nsplit);
+  dim3 grid(row_tiles(a.N), a.BH, a.nsplit * P1<TT, D>::NH);
   if constexpr (TT::KPL == 1) {
     hipError_t e = ensure_lds(&bob_pass1_simple_kernel<TT, D, CAUSAL>, lds);
     if (e != hipSuccess) return e;
@@ -578,7 +591,7 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_c1_t(const Pass1Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH);
+  dim3 grid(row_tiles(a.N), a.BH, P1<TT, D>::NH);
   hipLaunchKernelGGL((bob_pass1_combine_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

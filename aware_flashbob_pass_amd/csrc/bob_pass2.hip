@@ -189,6 +189,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
   constexpr int NT = 3, NBUF = 3;
   constexpr int STAGE_ELEMS = NT * G::ROW_ELEMS + 4 * kTile * 4 / (int)sizeof(T);  // tiles + 4 x 32 floats
+  // d = 64 forms the next step's score tiles during the current step; d = 128
+  // (no register room next to the resident K, V, UK, UV rows) forms them per step.
+  constexpr bool PIPE = D == 64;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     p_ = TT::mfma(ado, bv[t], p_);
     h_ = TT::mfma(ado, buv[t], h_);
   };
-  if (nsteps > 0 && active(0)) {
+  if (PIPE && nsteps > 0 && active(0)) {
 #pragma unroll
     for (int t = 0; t < DK; ++t) scores_kstep(0, t, sc, gc, pc, hc);
   }
@@ -284,6 +287,14 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     const int i0 = (it_begin + j) * kTile;
     f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
     if (act) {
+      if constexpr (!PIPE) {
+        sc = zero16();
+        gc = zero16();
+        pc = zero16();
+        hc = zero16();
+#pragma unroll
+        for (int t = 0; t < DK; ++t) scores_kstep(S, t, sc, gc, pc, hc);
+      }
       const float* sv = scal(S);
       float lqv[16], dqv[16], alv[16], eqv[16];
 #pragma unroll
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
       };
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        scores_kstep(SN, t, sx, gx, px, hx);  // stale (unused) on the last step
+        if constexpr (PIPE) scores_kstep(SN, t, sx, gx, px, hx);  // stale (unused) on the last step
 #pragma unroll
         for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
       }
@@ -342,14 +353,16 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
           accK[mb] = TT::mfma(tq, wsb[t], accK[mb]);
           accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);
         }
-    } else if (act_next) {
+    } else if (PIPE && act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) scores_kstep(SN, t, sx, gx, px, hx);
     }
-    sc = sx;
-    gc = gx;
-    pc = px;
-    hc = hx;
+    if constexpr (PIPE) {
+      sc = sx;
+      gc = gx;
+      pc = px;
+      hc = hx;
+    }
     wait_vmem();
     __syncthreads();
   };

@@ -57,6 +57,8 @@ struct BwdArgs {
 
 // Float count of one wave's partial record.
 __host__ __device__ inline size_t pass1_record_floats(int d) { return (size_t)(4 * (d / 32) * 16 + 2) * 64; }
+// 16-bit pass 1 at d = 128 splits the accumulated head dimension in halves.
+inline int pass1_halves(DT dt, int d) { return (dt != DT::F32 && d == 128) ? 2 : 1; }
 __host__ __device__ inline size_t fwd_record_floats(int d) { return (size_t)((d / 32) * 16 + 2) * 64; }
 __host__ __device__ inline size_t pass2_record_floats(int d) { return (size_t)(2 * (d / 32) * 16) * 64; }
 __host__ __device__ inline int row_tiles(int N) { return (N + kBlockRows - 1) / kBlockRows; }
