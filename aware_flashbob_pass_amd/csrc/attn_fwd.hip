@@ -73,10 +73,12 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  int qt, bh;
+  tile_and_head<CAUSAL, true>(qt, bh);
+  const int N = a.N, split = blockIdx.z;
   const size_t base = (size_t)bh * N * D;
   const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base};
-  const int q0 = blockIdx.x * kBlockRows + wave * kTile;
+  const int q0 = qt * kBlockRows + wave * kTile;
   const int qi = q0 + n;
 
   V bq[DK];
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   const float cs = a.tau * kLog2e;
 
   int nkt = (N + kTile - 1) / kTile;
-  if (CAUSAL) nkt = min(nkt, (int)(blockIdx.x + 1) * (kBlockRows / kTile));
+  if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
   const int kt_begin = (int)((long long)split * nkt / a.nsplit);
   const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
   const int nsteps = kt_end - kt_begin;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
     fwd_epilogue<TT, D, WITH_D>(acc, m, l, qi, g, bh, a);
     return;
   }
-  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + blockIdx.x) * 4 + wave;
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + qt) * 4 + wave;
   float* R = a.part + rec * fwd_record_floats(D);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) store_acc16(R + (mb * 64 + lane) * 16, acc[mb]);  // [MB][64 lanes][16]

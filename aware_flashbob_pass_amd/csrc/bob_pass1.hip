@@ -82,19 +82,19 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f
 
 // Raw accumulators and row partials of one wave for split `split`, half `half`.
 template <class TT, int D>
-__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int wave, int half) {
+__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int qt, int wave, int half) {
   constexpr int NH = P1<TT, D>::NH;
-  const size_t rec = ((((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave) * NH + half;
+  const size_t rec = ((((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave) * NH + half;
   return a.part + rec * pass1_record_floats(D / NH);
 }
 
 template <class TT, int D>
 __device__ inline void pass1_write_record(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
                                           const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
-                                          float alpha_p, float e0_p, int split, int bh, int wave, int lane, int half,
-                                          const Pass1Args& a) {
+                                          float alpha_p, float e0_p, int split, int bh, int qt, int wave, int lane,
+                                          int half, const Pass1Args& a) {
   constexpr int MB = P1<TT, D>::MBA;
-  float* R = pass1_record<TT, D>(a, split, bh, wave, half);
+  float* R = pass1_record<TT, D>(a, split, bh, qt, wave, half);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
     pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, 0, a);
     return;
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, 0, a);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, blockIdx.x, wave, lane, 0, a);
 }
 
 // Interleaving request for one pipelined pass-1 step (one basic block): each
@@ -289,11 +289,13 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y, split = blockIdx.z / NH, half = blockIdx.z % NH;
+  int qt, bh;
+  tile_and_head<CAUSAL, true>(qt, bh);
+  const int N = a.N, split = blockIdx.z / NH, half = blockIdx.z % NH;
   const size_t base = (size_t)bh * N * D;
   const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base,
                       reinterpret_cast<const T*>(a.UK) + base, reinterpret_cast<const T*>(a.UV) + base};
-  const int q0 = blockIdx.x * kBlockRows + wave * kTile;
+  const int q0 = qt * kBlockRows + wave * kTile;
   const int qi = q0 + n;
 
   V bq[DK], bdo[DK], buq[DK];
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   float alpha_p = 0.f, e0_p = 0.f;
 
   int nkt = (N + kTile - 1) / kTile;
-  if (CAUSAL) nkt = min(nkt, (int)(blockIdx.x + 1) * (kBlockRows / kTile));
+  if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
   const int kt_begin = (int)((long long)split * nkt / a.nsplit);
   const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
   const int nsteps = kt_end - kt_begin;
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, half, a);
     return;
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, wave, lane, half, a);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, half, a);
 }
 
 // Sum the split records of each wave in split order, then apply the epilogue.
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
   }
   float alpha_p = 0.f, e0_p = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) {
-    const float* R = pass1_record<TT, D>(a, sp, bh, wave, half);
+    const float* R = pass1_record<TT, D>(a, sp, bh, blockIdx.x, wave, half);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       A[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);

@@ -44,9 +44,9 @@ __device__ inline void pass2_epilogue(const f32x16 (&dK)[Geo<TT, D>::MB], const 
 
 template <class TT, int D>
 __device__ inline void pass2_write_record(const f32x16 (&dK)[Geo<TT, D>::MB], const f32x16 (&dV)[Geo<TT, D>::MB],
-                                          int split, int bh, int wave, int lane, const Pass2Args& a) {
+                                          int split, int bh, int kt, int wave, int lane, const Pass2Args& a) {
   constexpr int MB = Geo<TT, D>::MB;
-  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave;
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + kt) * 4 + wave;
   float* R = a.part + rec * pass2_record_floats(D);  // [2][MB][64 lanes][16]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);
     return;
   }
-  pass2_write_record<TT, D>(accK, accV, split, bh, wave, lane, a);
+  pass2_write_record<TT, D>(accK, accV, split, bh, blockIdx.x, wave, lane, a);
 }
 
 // Pipelined variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
@@ -198,13 +198,15 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
+  int kt, bh;
+  tile_and_head<CAUSAL, false>(kt, bh);
+  const int N = a.N, split = blockIdx.z;
   const size_t base = (size_t)bh * N * D;
   const size_t vbase = (size_t)bh * N;
   const T* src[NT] = {reinterpret_cast<const T*>(a.Q) + base, reinterpret_cast<const T*>(a.dO) + base,
                       reinterpret_cast<const T*>(a.UQ) + base};
   const float* vsrc[4] = {a.L + vbase, a.D + vbase, a.alpha + vbase, a.E + vbase};
-  const int k0w = blockIdx.x * kBlockRows + wave * kTile;
+  const int k0w = kt * kBlockRows + wave * kTile;
   const int kj = k0w + n;
 
   V bk[DK], bv[DK], buk[DK], buv[DK];
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   }
 
   const int nqt = (N + kTile - 1) / kTile;
-  const int qt_first = CAUSAL ? (int)blockIdx.x * (kBlockRows / kTile) : 0;
+  const int qt_first = CAUSAL ? kt * (kBlockRows / kTile) : 0;
   const int span = nqt - qt_first;
   const int it_begin = qt_first + (int)((long long)split * span / a.nsplit);
   const int it_end = qt_first + (int)((long long)(split + 1) * span / a.nsplit);
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);
     return;
   }
-  pass2_write_record<TT, D>(accK, accV, split, bh, wave, lane, a);
+  pass2_write_record<TT, D>(accK, accV, split, bh, kt, wave, lane, a);
 }
 
 template <class TT, int D>

@@ -312,6 +312,23 @@ __device__ inline f32x16 load_acc16(const float* src) {
   return v;
 }
 
+// Tile and head of a workgroup of a (tiles x heads) grid. Causal grids are
+// walked heaviest tile first across all heads (longest-processing-time order):
+// the dispatcher issues workgroups by linear id, so tile `heavy_first(lin)`
+// for every head comes before the next lighter tile of any head.
+template <bool CAUSAL, bool LAST_IS_HEAVIEST>
+__device__ inline void tile_and_head(int& tile, int& head) {
+  if (!CAUSAL) {
+    tile = blockIdx.x;
+    head = blockIdx.y;
+    return;
+  }
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int rank = lin / gridDim.y;
+  head = lin % gridDim.y;
+  tile = LAST_IS_HEAVIEST ? (int)gridDim.x - 1 - rank : rank;
+}
+
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
