@@ -19,3 +19,4 @@ from .binding import (  # noqa: F401
     set_tuning,
     workspace_bytes,
 )
+from .autograd import attention  # noqa: F401
