@@ -63,6 +63,81 @@ def traffic_from_profile():
     return s.get("hbm_bytes_per_launch")
 
 
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_kernel_mean(directory):
+    agg = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def digest_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
+    """HBM bytes per dispatch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) each scaled by the factor that makes the same counter read the true
+    size of a plain 512 MiB device copy (bench.py --calibrate-copy 512)."""
+    copy_bytes = 512 << 20
+    f, w = _per_kernel_mean(fetch_dir), _per_kernel_mean(write_dir)
+    cf, cw = _per_kernel_mean(copy_fetch_dir), _per_kernel_mean(copy_write_dir)
+    copy_name = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()][0]
+    ff = copy_bytes / (cf[copy_name] * 1024)
+    wf = copy_bytes / (cw[copy_name] * 1024)
+    kernels = {}
+    for k in f:
+        short = k.replace("void fb::", "").split("(")[0]
+        kernels[short] = {"fetch_kib": round(f[k], 1), "write_kib": round(w.get(k, 0.0), 1),
+                          "hbm_bytes": int(f[k] * 1024 * ff + w.get(k, 0.0) * 1024 * wf)}
+    p1 = [v for k, v in kernels.items() if k.startswith("bob_pass1_kernel<")]
+    summary = {
+        "workload": "long_16k: B=1,H=1,N=16384,d=64,bf16,non-causal",
+        "source_hash": pass1_source_hash(),
+        "copy_calibration": {"bytes": copy_bytes, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+        "hbm_bytes_per_launch": p1[0]["hbm_bytes"] if p1 else None,
+        "kernels": kernels,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d <FETCH> -o run --output-format csv -- python3 bench.py --steps 5 --warmup 2 "
+            "--no-cpu --no-endpoint --no-parity",
+            "rocprofv3 --pmc WRITE_SIZE -d <WRITE> -o run --output-format csv -- python3 bench.py --steps 5 --warmup 2 "
+            "--no-cpu --no-endpoint --no-parity",
+            "rocprofv3 --pmc FETCH_SIZE -d <COPY_FETCH> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+            "rocprofv3 --pmc WRITE_SIZE -d <COPY_WRITE> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+            "python3 bench.py --digest-pmc <FETCH> <WRITE> <COPY_FETCH> <COPY_WRITE> " + os.path.relpath(out, ROOT),
+        ],
+    }
+    with open(out, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps(summary, indent=1))
+
+
+def digest_trace(trace_dir, out):
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = ["# Kernel trace: BoB call at long_16k (B=1, H=1, N=16384, d=64, bf16, non-causal)", "",
+             "Commands (repository root, one MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py --steps 5 "
+             "--warmup 2 --no-cpu --no-endpoint --no-parity",
+             "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT), "```", "",
+             f"Pass-1 source hash (bob_pass1.hip + common.hpp + kernels.hpp): {pass1_source_hash()}", "",
+             "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"].replace("void fb::", "").split("(")[0]
+        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", "Calls include bench.py's 2 warm-up steps and its 5 untimed repeats (for the call time without "
+              "per-kernel events)."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, inputs, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: query rows [0, R) of head 0 against all N keys; extrapolate by N/R."""
@@ -114,7 +189,17 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
+    ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
+                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (csv dirs) into OUT (json)")
+    ap.add_argument("--digest-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run (csv dir) into OUT (markdown)")
     args = ap.parse_args()
+    if args.digest_pmc:
+        digest_pmc(*args.digest_pmc)
+        return
+    if args.digest_trace:
+        digest_trace(*args.digest_trace)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
