@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_fwd,
     bob_attention,
     bob_attention_alloc,
+    bob_attention_fourpass,
     bob_attention_with_stats,
     load_library,
     profile_start,

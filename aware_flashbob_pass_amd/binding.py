@@ -31,6 +31,7 @@ SIGNATURES = {
     "bob_attention": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "bob_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "bob_attention_ws": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P, _S, _P]),
+    "bob_attention_fourpass_ws": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P, _S, _P]),
     "bob_attention_with_stats": (_I, [_P] * 10 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 6 + [_P, _S, _P]),
     "attn_fwd": (_I, [_P] * 4 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 3 + [_P]),
     "attn_bwd": (_I, [_P] * 6 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
@@ -138,6 +139,22 @@ def bob_attention(q, k, v, do, uq, uk, uv, tau=None, causal=False, workspace=Non
     _check(lib.bob_attention_ws(*[_ptr(t) for t in (q, k, v, do, uq, uk, uv)], _tau(tau, d), int(bool(causal)),
                                 B, H, N, d, dt, *[_ptr(t) for t in outs], _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream()))
+    return tuple(outs)
+
+
+def bob_attention_fourpass(q, k, v, do, uq, uk, uv, tau=None, causal=False, workspace=None, out=None):
+    """The same BoB result through the four-pass ablation schedule (bf16/fp16)."""
+    ref = _check_inputs([("q", q), ("k", k), ("v", v), ("do", do), ("uq", uq), ("uk", uk), ("uv", uv)])
+    B, H, N, d = ref.shape
+    lib = load_library()
+    dt = _DT[ref.dtype]
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.bob_workspace_bytes(B, H, N, d, dt)), 1), dtype=torch.uint8,
+                                device=ref.device)
+    outs = [torch.empty_like(ref) for _ in range(4)] if out is None else list(out)
+    _check(lib.bob_attention_fourpass_ws(*[_ptr(t) for t in (q, k, v, do, uq, uk, uv)], _tau(tau, d),
+                                         int(bool(causal)), B, H, N, d, dt, *[_ptr(t) for t in outs],
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return tuple(outs)
 
 

@@ -173,6 +173,25 @@ fb_status_t run(const char* name, hipStream_t s, F&& launch) {
   return FB_OK;
 }
 
+// pass 2 (key-tile parallel) and its split reduction
+fb_status_t column_pass(const void* Q, const void* K, const void* V, const void* dO, const void* UQ, const void* UK,
+                        const void* UV, const float* L, const float* D, const float* alpha, const float* E, float tau,
+                        bool causal, int BH, int N, int d, DT dt, void* gK, void* gV, char* ws, const WsLayout& w,
+                        hipStream_t s) {
+  fb::Pass2Args p2{};
+  p2.Q = Q; p2.K = K; p2.V = V; p2.dO = dO; p2.UQ = UQ; p2.UK = UK; p2.UV = UV;
+  p2.L = L; p2.D = D; p2.alpha = alpha; p2.E = E; p2.gK = gK; p2.gV = gV;
+  p2.part = reinterpret_cast<float*>(ws + w.part);
+  p2.tau = tau; p2.N = N; p2.BH = BH; p2.nsplit = w.s2;
+  fb_status_t st = run("bob_pass2", s, [&] { return fb::launch_pass2(p2, dt, d, causal, s); });
+  if (st) return st;
+  if (w.s2 > 1) {
+    st = run("bob_pass2_reduce", s, [&] { return fb::launch_pass2_reduce(p2, dt, d, s); });
+    if (st) return st;
+  }
+  return FB_OK;
+}
+
 // pass 1 + pass 2 from O, L, D (all device pointers already checked)
 fb_status_t two_pass(const void* Q, const void* K, const void* V, const void* dO, const void* UQ, const void* UK,
                      const void* UV, const void* O, const float* L, const float* D, float tau, bool causal, int B,
@@ -191,18 +210,27 @@ fb_status_t two_pass(const void* Q, const void* K, const void* V, const void* dO
     st = run("bob_pass1_combine", s, [&] { return fb::launch_pass1_combine(p1, dt, d, s); });
     if (st) return st;
   }
-  fb::Pass2Args p2{};
-  p2.Q = Q; p2.K = K; p2.V = V; p2.dO = dO; p2.UQ = UQ; p2.UK = UK; p2.UV = UV;
-  p2.L = L; p2.D = D; p2.alpha = alpha; p2.E = E; p2.gK = gK; p2.gV = gV;
-  p2.part = reinterpret_cast<float*>(ws + w.part);
-  p2.tau = tau; p2.N = N; p2.BH = BH; p2.nsplit = w.s2;
-  st = run("bob_pass2", s, [&] { return fb::launch_pass2(p2, dt, d, causal, s); });
-  if (st) return st;
-  if (w.s2 > 1) {
-    st = run("bob_pass2_reduce", s, [&] { return fb::launch_pass2_reduce(p2, dt, d, s); });
+  return column_pass(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau, causal, BH, N, d, dt, gK, gV, ws, w, s);
+}
+
+// Four-pass ablation: alpha sweep, E sweep, row-output sweep, then pass 2.
+fb_status_t four_pass(const void* Q, const void* K, const void* V, const void* dO, const void* UQ, const void* UK,
+                      const void* UV, const void* O, const float* L, const float* D, float tau, bool causal, int B,
+                      int H, int N, int d, fb_dtype_t dtype, void* gQ, void* gK, void* gV, void* gdO, float* alpha,
+                      float* E, char* ws, const WsLayout& w, hipStream_t s) {
+  const DT dt = to_dt(dtype);
+  const int BH = B * H;
+  fb::Pass1Args p1{};
+  p1.Q = Q; p1.K = K; p1.V = V; p1.dO = dO; p1.UQ = UQ; p1.UK = UK; p1.UV = UV; p1.O = O;
+  p1.L = L; p1.D = D; p1.gQ = gQ; p1.gdO = gdO; p1.alpha = alpha; p1.E = E;
+  p1.part = reinterpret_cast<float*>(ws + w.part);
+  p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
+  static const char* names[3] = {"fourpass_alpha", "fourpass_energy", "fourpass_rows"};
+  for (int sweep = 0; sweep < 3; ++sweep) {
+    fb_status_t st = run(names[sweep], s, [&] { return fb::launch_fourpass_sweep(p1, sweep, dt, d, causal, s); });
     if (st) return st;
   }
-  return FB_OK;
+  return column_pass(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau, causal, BH, N, d, dt, gK, gV, ws, w, s);
 }
 
 }  // namespace
@@ -254,6 +282,40 @@ fb_status_t bob_attention_ws(const void* Q, const void* K, const void* V, const 
   }
   st = two_pass(Q, K, V, dO, UQ, UK, UV, O, L, D, tau, causal != 0, B, H, N, d, dtype, gQ, gK, gV, gdO,
                 reinterpret_cast<float*>(wsb + w.alpha), reinterpret_cast<float*>(wsb + w.e), wsb, w, stream);
+  if (st) return st;
+  return ok();
+}
+
+fb_status_t bob_attention_fourpass_ws(const void* Q, const void* K, const void* V, const void* dO, const void* UQ,
+                                      const void* UK, const void* UV, float tau, int causal, int B, int H, int N, int d,
+                                      fb_dtype_t dtype, void* gQ, void* gK, void* gV, void* gdO, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  fb_status_t st = check_shape(B, H, N, d, dtype, tau);
+  if (st) return st;
+  if (dtype == FB_F32) return fail(FB_ERR_DTYPE, "the four-pass schedule is implemented for bf16/fp16 inputs");
+  st = check_ptrs({{"Q", Q}, {"K", K}, {"V", V}, {"dO", dO}, {"UQ", UQ}, {"UK", UK}, {"UV", UV},
+                   {"gQ", gQ}, {"gK", gK}, {"gV", gV}, {"gdO", gdO}}, 16);
+  if (st) return st;
+  st = check_no_alias({{"gQ", gQ}, {"gK", gK}, {"gV", gV}, {"gdO", gdO}},
+                      {{"Q", Q}, {"K", K}, {"V", V}, {"dO", dO}, {"UQ", UQ}, {"UK", UK}, {"UV", UV}});
+  if (st) return st;
+  const WsLayout w = layout(B, H, N, d, dtype);
+  if (!ws) return fail(FB_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(FB_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < w.total) return fail(FB_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  char* wsb = static_cast<char*>(ws);
+  void* O = wsb + w.o;
+  float* L = reinterpret_cast<float*>(wsb + w.l);
+  float* D = reinterpret_cast<float*>(wsb + w.dd);
+  fb::FwdArgs fa{Q, K, V, dO, O, L, D, tau, N, B * H, w.s0, reinterpret_cast<float*>(wsb + w.part)};
+  st = run("attn_fwd_stats", stream, [&] { return fb::launch_attn_fwd(fa, to_dt(dtype), d, causal != 0, B * H, stream); });
+  if (st) return st;
+  if (w.s0 > 1) {
+    st = run("attn_fwd_combine", stream, [&] { return fb::launch_attn_fwd_combine(fa, to_dt(dtype), d, stream); });
+    if (st) return st;
+  }
+  st = four_pass(Q, K, V, dO, UQ, UK, UV, O, L, D, tau, causal != 0, B, H, N, d, dtype, gQ, gK, gV, gdO,
+                 reinterpret_cast<float*>(wsb + w.alpha), reinterpret_cast<float*>(wsb + w.e), wsb, w, stream);
   if (st) return st;
   return ok();
 }

@@ -236,6 +236,89 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
   pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, blockIdx.x, wave, lane, 0, a);
 }
 
+// ---- four-pass ablation schedule (modes of the pipelined kernel) -----------------
+enum : int { kTwoPass = 0, kAlphaPass = 1, kEnergyPass = 2, kRowsPass = 3 };
+
+// Record of one wave: the row partial (alpha or E sweeps) or the two row-output
+// accumulators (rows sweep), lane-contiguous.
+template <class TT, int D, int MODE>
+__device__ inline float* fourpass_record(const Pass1Args& a, int split, int bh, int qt, int wave) {
+  constexpr size_t REC = MODE == kRowsPass ? (size_t)2 * (D / 32) * 16 * 64 : 64;
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave;
+  return a.part + rec * REC;
+}
+
+template <class TT, int D, int MODE>
+__device__ inline void fourpass_epilogue(const f32x16 (&Q)[D / 32], const f32x16 (&X)[D / 32], float s_p, int qi,
+                                         int g, int bh, const Pass1Args& a) {
+  using T = typename TT::elem;
+  const float total = s_p + xor32(s_p);
+  if (qi >= a.N) return;
+  const size_t row = (size_t)bh * a.N + qi;
+  if constexpr (MODE == kAlphaPass) {
+    if (g == 0) a.alpha[row] = total;
+  } else if constexpr (MODE == kEnergyPass) {
+    if (g == 0) a.E[row] = total;
+  } else {
+    T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
+    T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
+    const float tau = a.tau;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = mb * 32 + kappa(r4 * 4, g);
+        const int r = r4 * 4;
+        store4<TT>(gQ + dim, tau * Q[mb][r], tau * Q[mb][r + 1], tau * Q[mb][r + 2], tau * Q[mb][r + 3]);
+        store4<TT>(gdO + dim, X[mb][r], X[mb][r + 1], X[mb][r + 2], X[mb][r + 3]);
+      }
+  }
+}
+
+template <class TT, int D, int MODE>
+__device__ inline void fourpass_write_record(const f32x16 (&Q)[D / 32], const f32x16 (&X)[D / 32], float s_p,
+                                             int split, int bh, int qt, int wave, int lane, const Pass1Args& a) {
+  float* R = fourpass_record<TT, D, MODE>(a, split, bh, qt, wave);
+  if constexpr (MODE == kRowsPass) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      store_acc16(R + ((0 * (D / 32) + mb) * 64 + lane) * 16, Q[mb]);
+      store_acc16(R + ((1 * (D / 32) + mb) * 64 + lane) * 16, X[mb]);
+    }
+  } else {
+    R[lane] = s_p;
+  }
+}
+
+template <class TT, int D, int MODE>
+__global__ __launch_bounds__(kBlock) void fourpass_combine_kernel(Pass1Args a) {
+  constexpr int MB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int bh = blockIdx.y;
+  const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
+  f32x16 Q[MB], X[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    Q[mb] = zero16();
+    X[mb] = zero16();
+  }
+  float s_p = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* R = fourpass_record<TT, D, MODE>(a, sp, bh, blockIdx.x, wave);
+    if constexpr (MODE == kRowsPass) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        Q[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+        X[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+      }
+    } else {
+      s_p += R[lane];
+    }
+  }
+  fourpass_epilogue<TT, D, MODE>(Q, X, s_p, qi, g, bh, a);
+}
+
 // Interleaving request for one pipelined pass-1 step (one basic block): each
 // matrix-core op is followed by a share of the element-wise vector work and by
 // the LDS reads of the NEXT k-step (operands are fetched one k-step ahead).
@@ -271,7 +354,14 @@ __device__ inline void pass1_schedule() {
 // formed on the matrix cores while the element-wise work of the current step
 // runs on the vector ALUs, and the accumulating contractions read their
 // transposed operands with the transposing LDS load (lds_tr_op).
-template <class TT, int D, bool CAUSAL>
+//
+// MODE selects the schedule: kTwoPass is the method's pass 1 above. The other
+// modes are the natural four-pass schedule that the affine structure collapses
+// (review page, Summary and Strengths on Prop. 4.1), kept for measuring what
+// the collapse saves: kAlphaPass sweeps the keys for alpha only (S and G),
+// kEnergyPass sweeps again for E with alpha known, and kRowsPass forms
+// gQ = tau (dS UK + Sbar K) and gdO = P UV + dPbar V with alpha and E known.
+template <class TT, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
@@ -282,7 +372,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   // d = 128 has no room for them next to 256 accumulator registers and forms
   // each step's score tiles at the start of the step instead.
   constexpr bool PIPE = D == 64;
-  constexpr int NH = P1<TT, D>::NH, MBA = P1<TT, D>::MBA;
+  constexpr bool TWO = MODE == kTwoPass;
+  constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
+  constexpr int NH = TWO ? P1<TT, D>::NH : 1;
+  constexpr int MBA = TWO ? P1<TT, D>::MBA : MB;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
@@ -307,6 +400,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   const float dq = a.D[rowv];
   const float cs = a.tau * kLog2e;
   const float tau = a.tau;
+  const float al = (MODE == kEnergyPass || MODE == kRowsPass) ? a.alpha[rowv] : 0.f;
+  const float er = MODE == kRowsPass ? a.E[rowv] : 0.f;
 
   f32x16 accA[MBA], accB[MBA], accC[MBA], accX[MBA];
 #pragma unroll
@@ -349,8 +444,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
       sc = TT::mfma(ak, bq[t], sc);
       gc = TT::mfma(ak, buq[t], gc);
       gc = TT::mfma(auk, bq[t], gc);
-      pc = TT::mfma(av, bdo[t], pc);
-      hc = TT::mfma(auv, bdo[t], hc);
+      if constexpr (NEED_DP) {
+        pc = TT::mfma(av, bdo[t], pc);
+        hc = TT::mfma(auv, bdo[t], hc);
+      }
     }
   }
 
@@ -388,8 +485,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           sc = TT::mfma(ak, bq[t], sc);
           gc = TT::mfma(ak, buq[t], gc);
           gc = TT::mfma(auk, bq[t], gc);
-          pc = TT::mfma(av, bdo[t], pc);
-          hc = TT::mfma(auv, bdo[t], hc);
+          if constexpr (NEED_DP) {
+            pc = TT::mfma(av, bdo[t], pc);
+            hc = TT::mfma(auv, bdo[t], hc);
+          }
         }
       }
       // log2-domain scores, masked where the key is out of range or after the query
@@ -406,18 +505,33 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
       auto elementwise = [&](int r) {
         const float p = fast_exp2(sc[r]);
         const float gv = gc[r] * tau;
-        const float dpv = pc[r];
-        const float t1 = dpv - dq;
-        const float vpg = p * gv;
-        const float vwb = p * fmaf(gv, t1, hc[r]);
-        alpha_p += vpg;
-        e0_p += vwb;
         const int kk = r >> 3, ss = r & 7;
-        vset<TT>(wa[kk], ss, p * t1);
-        vset<TT>(wb[kk], ss, vwb);
-        vset<TT>(pd[kk], ss, p * dpv);
-        vset<TT>(pp[kk], ss, p);
-        vset<TT>(pg[kk], ss, vpg);
+        if constexpr (MODE == kAlphaPass) {
+          alpha_p += p * gv;
+        } else if constexpr (MODE == kEnergyPass) {
+          const float dpv = pc[r];
+          e0_p += p * (fmaf(gv, dpv - dq, hc[r]) - al * dpv);  // P Pbar: E directly
+        } else if constexpr (MODE == kRowsPass) {
+          const float dpv = pc[r];
+          const float t1 = dpv - dq;
+          const float pbar = fmaf(gv, t1, hc[r]) - al * dpv;
+          vset<TT>(wa[kk], ss, p * t1);             // dS
+          vset<TT>(wb[kk], ss, p * (pbar - er));    // Sbar
+          vset<TT>(pp[kk], ss, p);                  // P
+          vset<TT>(pg[kk], ss, p * (gv - al));      // dPbar
+        } else {
+          const float dpv = pc[r];
+          const float t1 = dpv - dq;
+          const float vpg = p * gv;
+          const float vwb = p * fmaf(gv, t1, hc[r]);
+          alpha_p += vpg;
+          e0_p += vwb;
+          vset<TT>(wa[kk], ss, p * t1);
+          vset<TT>(wb[kk], ss, vwb);
+          vset<TT>(pd[kk], ss, p * dpv);
+          vset<TT>(pp[kk], ss, p);
+          vset<TT>(pg[kk], ss, vpg);
+        }
       };
       // phase 1: next step's score tiles (matrix cores) with rows 0..7 (vector ALUs);
       // the last step also forms "next" tiles from a stale stage, never used.
@@ -437,9 +551,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           const V(&o)[4] = ro[t & 1];
           sx = TT::mfma(o[0], bq[t], sx);
           gx = TT::mfma(o[0], buq[t], gx);
-          px = TT::mfma(o[1], bdo[t], px);
+          if constexpr (NEED_DP) px = TT::mfma(o[1], bdo[t], px);
           gx = TT::mfma(o[2], bq[t], gx);
-          hx = TT::mfma(o[3], bdo[t], hx);
+          if constexpr (NEED_DP) hx = TT::mfma(o[3], bdo[t], hx);
 #pragma unroll
           for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
         }
@@ -456,6 +570,11 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         o[2] = lds_tr_op<TT, D>(cv, mb, t, lane);
         o[3] = lds_tr_op<TT, D>(cuv, mb, t, lane);
       };
+      if constexpr (MODE == kAlphaPass || MODE == kEnergyPass) {
+        // scalar sweeps: no accumulating contractions
+#pragma unroll
+        for (int r = 8; r < 16; ++r) elementwise(r);
+      } else {
       if constexpr (PIPE) fetch_tr(0, to[0]);
 #pragma unroll
       for (int q = 0; q < NK * MBA; ++q) {
@@ -471,14 +590,22 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           for (int r = 8 + mb * 8 / MBA; r < 8 + (mb + 1) * 8 / MBA; ++r) elementwise(r);
         }
         const V(&o)[4] = to[q & 1];
-        accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);
-        accB[mb] = TT::mfma(o[0], pd[t], accB[mb]);
-        accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);
-        accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);
-        accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);
-        accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);
+        if constexpr (MODE == kRowsPass) {
+          accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);  // dS UK
+          accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);  // P UV
+          accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);  // Sbar K
+          accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);  // dPbar V
+        } else {
+          accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);
+          accB[mb] = TT::mfma(o[0], pd[t], accB[mb]);
+          accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);
+          accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);
+          accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);
+          accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);
+        }
       }
-      if constexpr (PIPE) pass1_schedule<DK, MBA>();
+      }
+      if constexpr (PIPE && TWO) pass1_schedule<DK, MBA>();
     } else if (PIPE && act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
@@ -489,8 +616,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         sx = TT::mfma(ak, bq[t], sx);
         gx = TT::mfma(ak, buq[t], gx);
         gx = TT::mfma(auk, bq[t], gx);
-        px = TT::mfma(av, bdo[t], px);
-        hx = TT::mfma(auv, bdo[t], hx);
+        if constexpr (NEED_DP) {
+          px = TT::mfma(av, bdo[t], px);
+          hx = TT::mfma(auv, bdo[t], hx);
+        }
       }
     }
     if constexpr (PIPE) {
@@ -514,11 +643,20 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   if (j < nsteps) step(I0{}, j);
   if (j + 1 < nsteps) step(I1{}, j + 1);
 
-  if (a.nsplit == 1) {
-    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, half, a);
-    return;
+  if constexpr (TWO) {
+    if (a.nsplit == 1) {
+      pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, half, a);
+      return;
+    }
+    pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, half, a);
+  } else {
+    const float sp = MODE == kAlphaPass ? alpha_p : e0_p;
+    if (a.nsplit == 1) {
+      fourpass_epilogue<TT, D, MODE>(accA, accX, sp, qi, g, bh, a);
+      return;
+    }
+    fourpass_write_record<TT, D, MODE>(accA, accX, sp, split, bh, qt, wave, lane, a);
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, half, a);
 }
 
 // Sum the split records of each wave in split order, then apply the epilogue.
@@ -570,9 +708,9 @@ static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bob_pass1_simple_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
   } else {
-    hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL>, lds);
+    hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL, kTwoPass>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL, kTwoPass>), grid, dim3(kBlock), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -603,6 +741,42 @@ hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s)
     case DT::BF16: return d == 64 ? launch_c1_t<BF16, 64>(a, s) : launch_c1_t<BF16, 128>(a, s);
     case DT::F16: return d == 64 ? launch_c1_t<F16, 64>(a, s) : launch_c1_t<F16, 128>(a, s);
     default: return d == 64 ? launch_c1_t<F32, 64>(a, s) : launch_c1_t<F32, 128>(a, s);
+  }
+}
+
+// ---- four-pass ablation launchers (16-bit inputs) ----------------------------
+template <class TT, int D, bool CAUSAL, int MODE>
+static hipError_t launch_fp_t(const Pass1Args& a, hipStream_t s) {
+  const size_t lds = pass1_lds_bytes<TT, D>();
+  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL, MODE>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bob_pass1_kernel<TT, D, CAUSAL, MODE>), dim3(row_tiles(a.N), a.BH, a.nsplit), dim3(kBlock), lds,
+                     s, a);
+  if ((e = hipGetLastError()) != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((fourpass_combine_kernel<TT, D, MODE>), dim3(row_tiles(a.N), a.BH), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class TT, int MODE>
+static hipError_t launch_fp_m(const Pass1Args& a, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? launch_fp_t<TT, 64, true, MODE>(a, s) : launch_fp_t<TT, 64, false, MODE>(a, s);
+  return causal ? launch_fp_t<TT, 128, true, MODE>(a, s) : launch_fp_t<TT, 128, false, MODE>(a, s);
+}
+
+template <class TT>
+static hipError_t launch_fp_tt(const Pass1Args& a, int sweep, int d, bool causal, hipStream_t s) {
+  switch (sweep) {
+    case 0: return launch_fp_m<TT, kAlphaPass>(a, d, causal, s);
+    case 1: return launch_fp_m<TT, kEnergyPass>(a, d, causal, s);
+    default: return launch_fp_m<TT, kRowsPass>(a, d, causal, s);
+  }
+}
+
+hipError_t launch_fourpass_sweep(const Pass1Args& a, int sweep, DT dt, int d, bool causal, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return launch_fp_tt<BF16>(a, sweep, d, causal, s);
+    case DT::F16: return launch_fp_tt<F16>(a, sweep, d, causal, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

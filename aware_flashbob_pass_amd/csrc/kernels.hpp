@@ -75,6 +75,10 @@ hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, 
 hipError_t launch_attn_fwd_combine(const FwdArgs& a, DT dt, int d, hipStream_t s);
 hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
+// Four-pass ablation schedule, 16-bit inputs: sweep 0 writes alpha, sweep 1 E
+// (alpha known), sweep 2 gQ and gdO (alpha and E known); each with its split merge.
+hipError_t launch_fourpass_sweep(const Pass1Args& a, int sweep, DT dt, int d, bool causal, hipStream_t s);
+__host__ __device__ inline size_t fourpass_record_floats(int d) { return (size_t)2 * (d / 32) * 16 * 64; }
 hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
 hipError_t launch_pass2_reduce(const Pass2Args& a, DT dt, int d, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& a, DT dt, int d, int BH, hipStream_t s);

@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "BoB ms/call + TFLOP/s (MFMA util) at N=16K,d=64 bf16; max N on 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
-UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12}
+UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12, "four_pass_exec": 27}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
 
 
@@ -187,6 +187,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-endpoint", action="store_true", help="skip the N=262144 feasibility call")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--schedule", choices=("two_pass", "four_pass"), default="two_pass",
+                    help="four_pass times the ablation schedule (separate alpha, E and row-output sweeps)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
@@ -234,9 +236,11 @@ def main():
     ws = torch.empty(max(1, fb.workspace_bytes(w.B, w.H, w.N, w.d, w.torch_dtype)), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(g["Q"]) for _ in range(4)]
 
+    call = fb.bob_attention if args.schedule == "two_pass" else fb.bob_attention_fourpass
+
     def step():
-        fb.bob_attention(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale, causal=w.causal,
-                         workspace=ws, out=outs)
+        call(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale, causal=w.causal,
+             workspace=ws, out=outs)
 
     for _ in range(args.warmup):
         step()
@@ -269,11 +273,15 @@ def main():
     tflops = UNITS["exec"] * unit / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kern = {k: {"launches": n, "avg_ms": t / max(n, 1)} for k, (n, t) in kernels.items()}
-    p1 = kern.get("bob_pass1", {"avg_ms": float("nan")})
-    p1_flops = UNITS["pass1"] * unit
+    # dominant kernel: pass 1 (11 units); for the four-pass ablation, its row-output sweep (9 units)
+    dom, dom_units = ("bob_pass1", UNITS["pass1"]) if args.schedule == "two_pass" else ("fourpass_rows", 9)
+    p1 = kern.get(dom, {"avg_ms": float("nan")})
+    p1_flops = dom_units * unit
     p1_tflops = p1_flops / (p1["avg_ms"] * 1e-3) / 1e12
     traffic = traffic_from_profile()
-    roofline = {"bound": "mfma", "kernel": "bob_pass1", "achieved": round(p1_tflops, 3), "peak": peak,
+    if args.schedule != "two_pass":
+        traffic = None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(p1_tflops, 3), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(p1_tflops / peak, 5), "traffic": traffic,
                 "algorithmic_flops_per_launch": p1_flops, "avg_launch_ms": p1["avg_ms"]}
 
@@ -291,9 +299,10 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "tau": w.scale, "seed": args.seed},
+                   "tau": w.scale, "seed": args.seed, "schedule": args.schedule},
         "roofline": roofline,
         "mfma_util": round(tflops / peak, 5),
+        "executed_units": UNITS["exec"] if args.schedule == "two_pass" else UNITS["four_pass_exec"],
         "ms_per_call_no_kernel_events": round(ms_clean, 5),
         "tflops_useful_12_units": round(UNITS["useful"] * unit / (ms * 1e-3) / 1e12, 3),
         "kernels": kern,

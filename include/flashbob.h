@@ -100,6 +100,22 @@ fb_status_t bob_attention_ws(const void* Q, const void* K, const void* V, const 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bob_attention_fourpass_ws: the same result as bob_attention_ws through the
+ * natural four-pass schedule that the method's affine structure collapses to
+ * two (review page, Summary; Strengths on Prop. 4.1): after the statistics
+ * kernel, one key sweep per query tile for alpha, a second for E (alpha
+ * known), a third for gQ and gdO (alpha and E known), then pass 2. It exists to
+ * measure what the collapse saves (an ablation). bf16/fp16 inputs only
+ * (FB_ERR_DTYPE for float32); same arguments, workspace and errors as
+ * bob_attention_ws.
+ */
+fb_status_t bob_attention_fourpass_ws(const void* Q, const void* K, const void* V, const void* dO,
+                                      const void* UQ, const void* UK, const void* UV,
+                                      float tau, int causal, int B, int H, int N, int d, fb_dtype_t dtype,
+                                      void* gQ, void* gK, void* gV, void* gdO,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * bob_attention_with_stats: pass 1 + pass 2 only, from saved statistics: the
  * forward output O ([B][H][N][d] dtype), the row LSE L and the row scalar
  * D = rowsum(dO * O) ([B][H][N] float32). This is the path whose device-memory

@@ -275,3 +275,28 @@ def test_workload_wide_64k():
 
 def test_workload_endpoint_256k():
     _rows_cols_check(workload.WORKLOADS["endpoint_256k"], 0, 32, 0)
+
+
+# ---- four-pass ablation schedule -----------------------------------------------
+@pytest.mark.parametrize("dtype,d,causal,N,splits", [("bf16", 64, False, 1000, None), ("bf16", 64, True, 777, None),
+                                                     ("bf16", 128, False, 300, None), ("fp16", 64, True, 257, None),
+                                                     ("bf16", 64, False, 1000, (3, 2)), ("bf16", 64, True, 17, None)])
+def test_fourpass_matches_oracle(dtype, d, causal, N, splits):
+    fb = _fb()
+    w = workload.custom(1, 2, N, d, dtype, causal)
+    cpu, g = _gpu_inputs(w, 21)
+    if splits:
+        fb.set_tuning(*splits)
+    try:
+        out = fb.bob_attention_fourpass(*[g[n] for n in workload.INPUT_NAMES], tau=w.scale, causal=causal)
+        two = _run_bob(fb, g, w)
+        torch.cuda.synchronize()
+    finally:
+        if splits:
+            fb.set_tuning(0, 0)
+    ref = _oracle_full(cpu, w)
+    errs = call_errors({k: to_f64(o.cpu()) for k, o in zip(OUTS, out)}, ref)
+    assert max(errs.values()) <= TOL[dtype], errs
+    # pass 2 is shared, and sees the same alpha/E up to rounding: the column outputs agree closely
+    for k in (1, 2):
+        assert rel(to_f64(out[k].cpu()), to_f64(two[k].cpu())) <= 1e-2
