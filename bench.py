@@ -176,6 +176,58 @@ def cpu_baseline(w, inputs, budget_s):
     }
 
 
+def hutchinson_bench(args, name):
+    """One Hutchinson sample of the attention Hessian diagonal, diag(H) ~ u * (H u)
+    with Rademacher u, where H is the Hessian of <dO, O(Q, K, V)> in (Q, K, V):
+    H u is BoB with U = u. Timed through the C ABI directly and through the
+    autograd integration (forward, create_graph backward, Hessian-vector
+    product), the way a Sophia-style optimizer samples it."""
+    import torch
+
+    import aware_flashbob_pass_amd as fb
+    import workload
+
+    w = workload.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = {k: v.to(dev) for k, v in workload.make_inputs(w, args.seed).items()}
+    shape = (w.B, w.H, w.N, w.d)
+    u = [workload.rademacher(shape, args.seed + 100 + i, w.torch_dtype).to(dev) for i in range(3)]
+    ws = torch.empty(max(1, fb.workspace_bytes(w.B, w.H, w.N, w.d, w.torch_dtype)), dtype=torch.uint8, device=dev)
+
+    def direct():
+        hu = fb.bob_attention(inp["Q"], inp["K"], inp["V"], inp["dO"], u[0], u[1], u[2], tau=w.scale,
+                              causal=w.causal, workspace=ws)
+        return [a * b for a, b in zip(u, hu[:3])]
+
+    q, k, v = (inp[n].clone().requires_grad_(True) for n in ("Q", "K", "V"))
+
+    def through_autograd():
+        o = fb.attention(q, k, v, tau=w.scale, causal=w.causal)
+        grads = torch.autograd.grad(o, (q, k, v), grad_outputs=inp["dO"], create_graph=True)
+        hu = torch.autograd.grad(grads, (q, k, v), grad_outputs=tuple(u))
+        return [a * b for a, b in zip(u, hu)]
+
+    res = {}
+    for label, fn in (("direct", direct), ("autograd", through_autograd)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        res[label] = start.elapsed_time(stop) / args.steps
+    print(json.dumps({
+        "metric": "Hutchinson Hessian-diagonal sample time, attention block", "value": round(res["autograd"], 5),
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_direct_c_abi": round(res["direct"], 5), "ms_through_autograd": round(res["autograd"], 5),
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "probe": "rademacher"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +239,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-endpoint", action="store_true", help="skip the N=262144 feasibility call")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--hutchinson", action="store_true",
+                    help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
     ap.add_argument("--schedule", choices=("two_pass", "four_pass"), default="two_pass",
                     help="four_pass times the ablation schedule (separate alpha, E and row-output sweeps)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -228,6 +282,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4, "launches": 5}))
+        return
+    if args.hutchinson:
+        hutchinson_bench(args, "gpt2_hessian" if args.workload == "long_16k" else args.workload)
         return
     w = workload.WORKLOADS[args.workload]
     log(f"bench: {w.describe()} steps={args.steps} warmup={args.warmup}")

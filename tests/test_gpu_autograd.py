@@ -63,3 +63,23 @@ def test_hessian_vector_product_is_bob():
     for a, b, key in zip(hv, direct[:3], ("gQ", "gK", "gV")):
         assert rel(to_f64(a.cpu()), ref[key]) <= TOL["bf16"]
         assert rel(to_f64(a.cpu()), to_f64(b.cpu())) <= 5e-3
+
+
+def test_hutchinson_sample_matches_oracle():
+    """diag(H) sample u * (H u) with Rademacher u, through the autograd path."""
+    import aware_flashbob_pass_amd as fb
+
+    w = workload.custom(2, 2, 200, 64, "bf16", True, sigma={"V": 0.1, "dO": 0.1})
+    cpu = workload.make_inputs(w, 13)
+    us = [workload.rademacher((2, 2, 200, 64), 50 + i, torch.bfloat16) for i in range(3)]
+    g = {k: v.cuda() for k, v in cpu.items()}
+    q, k, v = (g[n].clone().requires_grad_(True) for n in ("Q", "K", "V"))
+    o = fb.attention(q, k, v, tau=w.scale, causal=True)
+    grads = torch.autograd.grad(o, (q, k, v), grad_outputs=g["dO"], create_graph=True)
+    hu = torch.autograd.grad(grads, (q, k, v), grad_outputs=tuple(x.cuda() for x in us))
+    torch.cuda.synchronize()
+    arrs = [to_f64(cpu[n]) for n in ("Q", "K", "V", "dO")] + [to_f64(x) for x in us]
+    ref = oracle.bob(*arrs, w.scale, True)
+    for got, u, key in zip(hu, us, ("gQ", "gK", "gV")):
+        est = to_f64(got.cpu()) * to_f64(u)
+        assert rel(est, ref[key] * to_f64(u)) <= TOL["bf16"], key

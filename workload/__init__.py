@@ -72,6 +72,13 @@ def make_inputs(w, seed=0):
     return out
 
 
+def rademacher(shape, seed, dtype=torch.float32):
+    """Seeded +-1 draws (for Hutchinson probes), exact in every supported dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    return (torch.randint(0, 2, shape, generator=gen, dtype=torch.int8) * 2 - 1).to(dtype)
+
+
 def custom(B, H, N, d, dtype="fp32", causal=False, sigma=None, tau=None, name="custom"):
     """A workload of any shape with the same recipe (used by parity sweeps)."""
     return Workload(name, B, H, N, d, dtype, causal, dict(sigma or {}), tau)
