@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_kernel(BwdArgs a) {
   T* v_r = k_r + G::ROW_ELEMS;
   T* k_t = v_r + G::ROW_ELEMS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int N = a.N, bh = blockIdx.y;
   const size_t base = (size_t)bh * N * D;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_kernel(BwdArgs a) {
   T* do_t = q_t + G::T_ELEMS;
   float* sc = reinterpret_cast<float*>(do_t + G::T_ELEMS);  // [2][32]: L*log2e, D
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int N = a.N, bh = blockIdx.y;
   const size_t base = (size_t)bh * N * D;

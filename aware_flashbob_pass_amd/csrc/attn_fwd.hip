@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   int qt, bh;
   tile_and_head<CAUSAL, true>(qt, bh);
@@ -194,7 +194,7 @@ template <class TT, int D, bool WITH_D>
 __global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
   constexpr int MB = G::MB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_simple_kernel(FwdArgs a) {
   T* krow = reinterpret_cast<T*>(smem);
   T* vt = krow + G::ROW_ELEMS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int N = a.N, bh = blockIdx.y;
   const size_t base = (size_t)bh * N * D;

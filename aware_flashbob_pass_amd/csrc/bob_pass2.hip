@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
   T* uq_t = do_t + G::T_ELEMS;
   float* sc = reinterpret_cast<float*>(uq_t + G::T_ELEMS);  // [4][32]: L*log2e, D, alpha, E
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int N = a.N, bh = blockIdx.y, split = blockIdx.z;
   const size_t base = (size_t)bh * N * D;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   int kt, bh;
   tile_and_head<CAUSAL, false>(kt, bh);
@@ -391,7 +391,7 @@ template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
   using G = Geo<TT, D>;
   constexpr int MB = G::MB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int kj = blockIdx.x * kBlockRows + wave * kTile + n;

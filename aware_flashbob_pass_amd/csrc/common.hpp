@@ -286,6 +286,10 @@ __device__ inline typename TT::vec lds_tr_op(const typename TT::elem* rowbuf, in
   return __builtin_bit_cast(typename TT::vec, v);
 }
 
+// Index of the calling wave in its workgroup as a wave-uniform (scalar)
+// value, so that branches and offsets derived from it stay scalar.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 __device__ inline f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -1,0 +1,97 @@
+// Pass-1 accumulator epilogue and split records, shared by the pass-1 kernels.
+//
+// FlashBoB review page (Summary; Strengths on Prop. 4.1): alpha and E enter
+// gQ and gdO affinely, so each query row keeps alpha-free sums over the keys
+// and applies the two scalars once at the end:
+//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i (P dP) K - E_i P K ],
+//   gdO_i = (P UV + (P G) V) - alpha_i O_i,   E_i = sum_j W_b - alpha_i D_i.
+// A = W_a UK + W_b K, B = (P dP) K, C = P K and X = P UV + (P G) V are the
+// four float32 register tiles (head dims x 32 queries per wave).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fb {
+
+template <class TT, int D>
+struct P1 {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  // 16-bit d = 128: each workgroup accumulates one half of the head dimension
+  // (the grid's z axis holds split x half); everything else accumulates all of it.
+  static constexpr int NH = (TT::KPL == 8 && D == 128) ? 2 : 1;
+  static constexpr int MBA = G::MB / NH;  // accumulated 32-wide head-dim blocks
+  // record layout (floats): acc[4][MBA][64 lanes][16], alpha_p[64], e0_p[64]
+  static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
+};
+
+// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave (head-dim
+// blocks half * MBA .. half * MBA + MBA - 1).
+template <class TT, int D>
+__device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
+                                      const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
+                                      float alpha_p, float e0_p, int qi, int g, int bh, int half,
+                                      const Pass1Args& a) {
+  using T = typename TT::elem;
+  constexpr int MBA = P1<TT, D>::MBA;
+  const int N = a.N;
+  const float alpha = alpha_p + xor32(alpha_p);
+  const float e0 = e0_p + xor32(e0_p);
+  if (qi >= N) return;
+  const size_t row = (size_t)bh * N + qi;
+  const float dq = a.D[row];
+  const float E = e0 - alpha * dq;
+  const T* O = reinterpret_cast<const T*>(a.O) + row * D;
+  T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
+  T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
+  const float tau = a.tau;
+#pragma unroll
+  for (int mbl = 0; mbl < MBA; ++mbl)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = (half * MBA + mbl) * 32 + kappa(r4 * 4, g);
+      float o[4], q[4], x[4];
+      load4<TT>(O + dim, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r4 * 4 + e;
+        q[e] = tau * (A[mbl][r] - alpha * B[mbl][r] - E * C[mbl][r]);
+        x[e] = X[mbl][r] - alpha * o[e];
+      }
+      store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
+      store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
+    }
+  if (g == 0 && half == 0) {
+    a.alpha[row] = alpha;
+    a.E[row] = E;
+  }
+}
+
+// Raw accumulators and row partials of one wave for split `split`, half `half`.
+template <class TT, int D>
+__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int qt, int wave, int half) {
+  constexpr int NH = P1<TT, D>::NH;
+  const size_t rec = ((((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave) * NH + half;
+  return a.part + rec * pass1_record_floats(D / NH);
+}
+
+template <class TT, int D>
+__device__ inline void pass1_write_record(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
+                                          const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
+                                          float alpha_p, float e0_p, int split, int bh, int qt, int wave, int lane,
+                                          int half, const Pass1Args& a) {
+  constexpr int MB = P1<TT, D>::MBA;
+  float* R = pass1_record<TT, D>(a, split, bh, qt, wave, half);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);
+    store_acc16(R + ((1 * MB + mb) * 64 + lane) * 16, B[mb]);
+    store_acc16(R + ((2 * MB + mb) * 64 + lane) * 16, C[mb]);
+    store_acc16(R + ((3 * MB + mb) * 64 + lane) * 16, X[mb]);
+  }
+  R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
+  R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;
+}
+
+}  // namespace fb

@@ -31,6 +31,7 @@ METRIC = "BoB ms/call + TFLOP/s (MFMA util) at N=16K,d=64 bf16; max N on 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12, "four_pass_exec": 27}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
+PASS1_SOURCES = ("bob_pass1.hip", "pass1_common.hpp", "common.hpp", "kernels.hpp")
 
 
 def flop_unit(w):
@@ -44,7 +45,7 @@ def log(msg):
 
 def pass1_source_hash():
     h = hashlib.sha256()
-    for f in ("bob_pass1.hip", "common.hpp", "kernels.hpp"):
+    for f in PASS1_SOURCES:
         with open(os.path.join(ROOT, "aware_flashbob_pass_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -125,7 +126,7 @@ def digest_trace(trace_dir, out):
              "rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py --steps 5 "
              "--warmup 2 --no-cpu --no-endpoint --no-parity",
              "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT), "```", "",
-             f"Pass-1 source hash (bob_pass1.hip + common.hpp + kernels.hpp): {pass1_source_hash()}", "",
+             f"Pass-1 source hash ({' + '.join(PASS1_SOURCES)}): {pass1_source_hash()}", "",
              "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
     for r in rows:
         n = r["Name"].replace("void fb::", "").split("(")[0]
