@@ -23,7 +23,7 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
   using T = typename TT::elem;
   const int N = a.N;
   const size_t base = (size_t)bh * N * D;
-  const float lt = l + xor32(l);
+  const float lt = pair_sum32(l);
   const float inv = 1.f / lt;
   if (qi >= N) return;
   T* O = reinterpret_cast<T*>(a.O) + base + (size_t)qi * D;
@@ -48,7 +48,7 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
   // lanes n and n + 32 own the same query, so the exchange stays paired
   if (g == 0) a.L[(size_t)bh * N + qi] = m * kLn2 + __logf(lt);
   if constexpr (WITH_D) {
-    dot += xor32(dot);
+    dot = pair_sum32(dot);
     if (g == 0) a.D[(size_t)bh * N + qi] = dot;
   }
 }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
       float mx = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = fmaxf(mx, xor32(mx));
+      mx = pair_max32(mx);
       const float mnew = fmaxf(m, mx);
       if (__ballot(mnew > m)) {
         const float f = fast_exp2(m - mnew);
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_simple_kernel(FwdArgs a) {
       s[r] = ok ? s[r] * cs : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair_max32(mx);
     const float mnew = fmaxf(m, mx);
     const float sc = fast_exp2(m - mnew);
     l *= sc;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_simple_kernel(FwdArgs a) {
       for (int t = 0; t < G::NK; ++t) acc[mb] = TT::mfma(lds_t_op<TT, D>(vt, mb * 32 + n, t, g), pp[t], acc[mb]);
   }
 
-  const float lt = l + xor32(l);
+  const float lt = pair_sum32(l);
   const float inv = 1.f / lt;
   if (qi < N) {
     T* O = reinterpret_cast<T*>(a.O) + base + (size_t)qi * D;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_simple_kernel(FwdArgs a) {
     // lanes n and n + 32 own the same query, so the exchanges below stay paired
     if (g == 0) a.L[(size_t)bh * N + qi] = m * kLn2 + __logf(lt);
     if constexpr (WITH_D) {
-      dot += xor32(dot);
+      dot = pair_sum32(dot);
       if (g == 0) a.D[(size_t)bh * N + qi] = dot;
     }
   }

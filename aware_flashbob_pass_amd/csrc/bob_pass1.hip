@@ -173,7 +173,7 @@ template <class TT, int D, int MODE>
 __device__ inline void fourpass_epilogue(const f32x16 (&Q)[D / 32], const f32x16 (&X)[D / 32], float s_p, int qi,
                                          int g, int bh, const Pass1Args& a) {
   using T = typename TT::elem;
-  const float total = s_p + xor32(s_p);
+  const float total = pair_sum32(s_p);
   if (qi >= a.N) return;
   const size_t row = (size_t)bh * a.N + qi;
   if constexpr (MODE == kAlphaPass) {

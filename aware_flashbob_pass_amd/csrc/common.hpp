@@ -333,7 +333,20 @@ __device__ inline void tile_and_head(int& tile, int& head) {
   tile = LAST_IS_HEAVIEST ? (int)gridDim.x - 1 - rank : rank;
 }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Sum / maximum of x over the lane pair (l, l ^ 32), returned on both lanes.
+// gfx950's v_permlane32_swap exchanges the two 32-lane halves in the vector ALU
+// (no LDS round trip): with both operands x, lane i < 32 receives (x[i],
+// x[i + 32]) and lane i >= 32 receives (x[i - 32], x[i]) (layout checked with an
+// in-bounds probe). Addition and maximum commute, so both lanes of a pair get
+// the bitwise-same result.
+__device__ inline float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -36,8 +36,8 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f
   using T = typename TT::elem;
   constexpr int MBA = P1<TT, D>::MBA;
   const int N = a.N;
-  const float alpha = alpha_p + xor32(alpha_p);
-  const float e0 = e0_p + xor32(e0_p);
+  const float alpha = pair_sum32(alpha_p);
+  const float e0 = pair_sum32(e0_p);
   if (qi >= N) return;
   const size_t row = (size_t)bh * N + qi;
   const float dq = a.D[row];
