@@ -297,25 +297,18 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
 #pragma unroll
         for (int t = 0; t < DK; ++t) scores_kstep(S, t, sc, gc, pc, hc);
       }
+      // Row scalars of the streamed queries: lane group g holds rows kappa(r, g), which
+      // for r = 4 r4 .. 4 r4 + 3 are the 4 consecutive rows 8 r4 + 4 g .. + 3.
       const float* sv = scal(S);
-      float lqv[16], dqv[16], alv[16], eqv[16];
+      auto row4 = [&](int which, int r4) {
+        return *reinterpret_cast<const f32x4*>(sv + which * kTile + r4 * 8 + g * 4);
+      };
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int q = r4 * 8 + g * 4;  // rows kappa(4 r4 .. 4 r4 + 3, g)
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sv + q);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sv + kTile + q);
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sv + 2 * kTile + q);
-        const f32x4 e4 = *reinterpret_cast<const f32x4*>(sv + 3 * kTile + q);
+        const f32x4 l4 = row4(0, r4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lqv[r4 * 4 + e] = l4[e];
-          dqv[r4 * 4 + e] = d4[e];
-          alv[r4 * 4 + e] = a4[e];
-          eqv[r4 * 4 + e] = e4[e];
-        }
+        for (int e = 0; e < 4; ++e) sc[r4 * 4 + e] = sc[r4 * 4 + e] * cs - l4[e];
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = sc[r] * cs - lqv[r];
       if (i0 + kTile > N || (CAUSAL && i0 < k0w + kTile - 1)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -324,15 +317,22 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
         }
       }
       V wds[NK], wsb[NK], wdp[NK];
+      f32x4 d4, a4, e4;  // D, alpha, E of the current group of 4 rows (loaded at its first row)
       auto elementwise = [&](int r) {
+        if ((r & 3) == 0) {
+          d4 = row4(1, r >> 2);
+          a4 = row4(2, r >> 2);
+          e4 = row4(3, r >> 2);
+        }
+        const float dq = d4[r & 3], al = a4[r & 3], eq = e4[r & 3];
         const float p = fast_exp2(sc[r]);
         const float gv = gc[r] * tau;
         const float dpv = pc[r];
-        const float t1 = dpv - dqv[r];
+        const float t1 = dpv - dq;
         const int kk = r >> 3, ss = r & 7;
         vset<TT>(wds[kk], ss, p * t1);
-        vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(alv[r], dpv, eqv[r])));
-        vset<TT>(wdp[kk], ss, p * (gv - alv[r]));
+        vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(al, dpv, eq)));
+        vset<TT>(wdp[kk], ss, p * (gv - al));
       };
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
