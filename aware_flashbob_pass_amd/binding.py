@@ -36,7 +36,7 @@ SIGNATURES = {
     "attn_fwd": (_I, [_P] * 4 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 3 + [_P]),
     "attn_bwd": (_I, [_P] * 6 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "fb_set_tuning": (_I, [_I, _I]),
-    "fb_profile_start": (None, []),
+    "fb_profile_start": (None, [ctypes.c_char_p]),
     "fb_profile_stop": (_I, [ctypes.POINTER(KernelTime), _I]),
 }
 
@@ -218,8 +218,9 @@ def attn_bwd(q, k, v, o, do, lse, tau=None, causal=False):
     return (*outs, dvec)
 
 
-def profile_start():
-    load_library().fb_profile_start()
+def profile_start(only=None):
+    """Record HIP events around every later launch (only those of kernel `only`, if given)."""
+    load_library().fb_profile_start(only.encode() if only else None)
 
 
 def profile_stop(max_kernels=32):

@@ -70,6 +70,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // empty: every kernel
 std::vector<ProfRec> g_prof;
 
 template <class F>
@@ -77,7 +78,7 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   bool on;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    on = g_prof_on;
+    on = g_prof_on && (g_prof_only.empty() || g_prof_only == name);
   }
   if (!on) return launch();
   hipEvent_t a = nullptr, b = nullptr;
@@ -437,8 +438,9 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   return ok();
 }
 
-void fb_profile_start(void) {
+void fb_profile_start(const char* only) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = only ? only : "";
   for (auto& r : g_prof) {
     hipEventDestroy(r.a);
     hipEventDestroy(r.b);

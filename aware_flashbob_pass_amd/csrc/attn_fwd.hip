@@ -61,7 +61,7 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // With `nsplit` > 1 each split covers a key range and writes a record
 // (accumulators, max, partial denominators) that fwd_combine merges.
 template <class TT, int D, bool CAUSAL, bool WITH_D>
-__global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
@@ -88,6 +88,8 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
   for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
   float m = -1e30f, l = 0.f;
   const float cs = a.tau * kLog2e;
+  const bool fold = cs > 0.f;           // wave-uniform
+  const float cm = fold ? cs : 1.f;     // multiplier of the score in the exponent
 
   int nkt = (N + kTile - 1) / kTile;
   if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
@@ -121,8 +123,14 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
     const int k0 = (kt_begin + j) * kTile;
     f32x16 sx = zero16();
     if (act) {
+      // With cs > 0 the scale stays folded into the exponent (p = 2^(raw cs - m)): the
+      // maximum of the raw scores times cs equals the maximum of the scaled scores
+      // (rounding is monotonic) and masked raw scores of -inf still give p = 0. With
+      // cs <= 0 the scores are scaled first and the exponent multiplies by 1.
+      if (!fold) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] *= cs;
+        for (int r = 0; r < 16; ++r) sc[r] *= cs;
+      }
       if (k0 + kTile > N || (CAUSAL && k0 + kTile - 1 > q0)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -130,9 +138,8 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
           if (!(key < N && (!CAUSAL || key <= qi))) sc[r] = -INFINITY;
         }
       }
-      float mx = sc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      float mx = max16(sc);
+      if (fold) mx *= cs;
       mx = pair_max32(mx);
       const float mnew = fmaxf(m, mx);
       if (__ballot(mnew > m)) {
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_fwd_kernel(FwdArgs a) {
         sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);  // stale on the last step
 #pragma unroll
         for (int r = t * 16 / DK; r < (t + 1) * 16 / DK; ++r) {
-          const float p = fast_exp2(sc[r] - m);
+          const float p = fast_exp2(fmaf(sc[r], cm, -m));
           l += p;
           vset<TT>(pp[r >> 3], r & 7, p);
         }

@@ -333,6 +333,16 @@ __device__ inline void tile_and_head(int& tile, int& head) {
   tile = LAST_IS_HEAVIEST ? (int)gridDim.x - 1 - rank : rank;
 }
 
+// Maximum of the 16 slots of one lane (balanced tree: depth 4).
+__device__ inline float max16(const f32x16& v) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = fmaxf(v[2 * i], v[2 * i + 1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = fmaxf(a[2 * i], a[2 * i + 1]);
+  return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+}
+
 // Sum / maximum of x over the lane pair (l, l ^ 32), returned on both lanes.
 // gfx950's v_permlane32_swap exchanges the two 32-lane halves in the vector ALU
 // (no LDS round trip): with both operands x, lane i < 32 receives (x[i],

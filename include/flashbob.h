@@ -167,11 +167,13 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
 fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits);
 
 /*
- * Kernel timing: fb_profile_start() makes every later launch record a pair of
- * HIP events on the stream it is launched on; fb_profile_stop() waits for
- * them, writes up to `max` entries (kernel name, launches, total ms) and
- * turns recording off. Returns the number of distinct kernels (may exceed
- * max), or a negative status.
+ * Kernel timing: fb_profile_start(only) makes every later launch of the
+ * kernel named `only` (every launch when `only` is NULL or "") record a pair
+ * of HIP events on the stream it is launched on; the string is copied.
+ * Restricting the events to one kernel keeps the timing of the others
+ * undisturbed. fb_profile_stop() waits for them, writes up to `max` entries
+ * (kernel name, launches, total ms) and turns recording off. Returns the
+ * number of distinct kernels (may exceed max), or a negative status.
  */
 typedef struct {
   char name[48];
@@ -179,7 +181,7 @@ typedef struct {
   double total_ms;
 } fb_kernel_time_t;
 
-void fb_profile_start(void);
+void fb_profile_start(const char* only);
 int fb_profile_stop(fb_kernel_time_t* out, int max);
 
 #ifdef __cplusplus

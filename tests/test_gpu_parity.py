@@ -118,6 +118,15 @@ def test_bob_splits_fp32_tight():
     _check_full(workload.custom(1, 1, 700, 64, "fp32", True), splits=(3, 4))
 
 
+@pytest.mark.parametrize("tau", [0.3, -0.125, 0.0])
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, False), ("bf16", 64, True), ("bf16", 128, True),
+                                            ("fp32", 64, True)])
+def test_bob_any_tau(tau, dtype, d, causal):
+    """Any finite scale: not a power of two, negative, and zero (uniform softmax; the
+    exact gQ and gK are then zero and are measured on the scale of gV and gdO)."""
+    _check_full(workload.custom(1, 2, 300, d, dtype, causal, tau=tau))
+
+
 def test_bob_deterministic():
     fb = _fb()
     w = workload.custom(1, 2, 777, 64, "bf16", False)
