@@ -54,12 +54,14 @@ int auto_splits(int BH, int N, int target = kTargetBlocks) {
   return std::max(1, std::min(s, kMaxSplits));
 }
 
-// The statistics kernel fits two workgroups per compute unit, so by default it
-// splits to fill 512; with an explicit pass-1 split it follows that value.
-void splits_for(int BH, int N, int* s0, int* s1, int* s2) {
+// Default split targets follow how many workgroups of each kernel one compute
+// unit holds: the statistics kernel at least two (512 workgroups); 16-bit pass 2
+// at d = 64 two (it is built for two waves per SIMD); pass 1 and the rest one.
+// With an explicit pass-1 split the statistics kernel follows that value.
+void splits_for(int BH, int N, fb::DT dt, int d, int* s0, int* s1, int* s2) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   *s1 = g_split1 > 0 ? g_split1 : auto_splits(BH, N);
-  *s2 = g_split2 > 0 ? g_split2 : auto_splits(BH, N);
+  *s2 = g_split2 > 0 ? g_split2 : auto_splits(BH, N, fb::pass2_blocks_per_cu(dt, d) * kTargetBlocks);
   *s0 = g_split1 > 0 ? g_split1 : auto_splits(BH, N, 2 * kTargetBlocks);
 }
 
@@ -143,7 +145,7 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   WsLayout w{};
   const size_t BH = (size_t)B * H;
   const size_t vec = align256(BH * N * sizeof(float));
-  splits_for((int)BH, N, &w.s0, &w.s1, &w.s2);
+  splits_for((int)BH, N, to_dt(dtype), d, &w.s0, &w.s1, &w.s2);
   if (dtype == FB_F32) w.s0 = 1;  // the float32 statistics kernel does not split
   size_t off = 0;
   w.o = off;

@@ -177,21 +177,21 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
   pass2_write_record<TT, D>(accK, accV, split, bh, blockIdx.x, wave, lane, a);
 }
 
-// Pipelined variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
-// tiles plus their four row scalars, prefetched two steps ahead; the next
-// step's score tiles are formed on the matrix cores while the current step's
-// weights are computed; transposed operands come from the transposing LDS load.
+// Staged variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
+// tiles plus their four row scalars, loaded two steps ahead; transposed
+// operands come from the transposing LDS load. Each step forms its score tiles,
+// its weights and its accumulating products in turn. At d = 64 the kernel fits
+// 256 registers, so two waves share each SIMD (two workgroups per CU) and each
+// one's matrix-core work overlaps the other's vector work; that beat forming
+// the next step's tiles during the current step at one wave per SIMD.
 template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
+__global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pass2Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
   constexpr int NT = 3, NBUF = 3;
   constexpr int STAGE_ELEMS = NT * G::ROW_ELEMS + 4 * kTile * 4 / (int)sizeof(T);  // tiles + 4 x 32 floats
-  // d = 64 forms the next step's score tiles during the current step; d = 128
-  // (no register room next to the resident K, V, UK, UV rows) forms them per step.
-  constexpr bool PIPE = D == 64;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
   wait_vmem();
   __syncthreads();
 
-  f32x16 sc = zero16(), gc = zero16(), pc = zero16(), hc = zero16();
+  f32x16 sc, gc, pc, hc;  // score tiles of the current step
   auto scores_kstep = [&](int j, int t, f32x16& s_, f32x16& g_, f32x16& p_, f32x16& h_) {
     const V aq = lds_row_op<TT, D>(tile(j, 0), n, t, g);
     const V ado = lds_row_op<TT, D>(tile(j, 1), n, t, g);
@@ -271,32 +271,21 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
     p_ = TT::mfma(ado, bv[t], p_);
     h_ = TT::mfma(ado, buv[t], h_);
   };
-  if (PIPE && nsteps > 0 && active(0)) {
-#pragma unroll
-    for (int t = 0; t < DK; ++t) scores_kstep(0, t, sc, gc, pc, hc);
-  }
-
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
-    constexpr int SN = (S + 1) % NBUF;
     if (j + 2 < nsteps) {  // buffer (S + 2) % NBUF was last read in step j - 1
       issue((S + 2) % NBUF, j + 2);
       put_scal((S + 2) % NBUF);
     }
     if (j + 3 < nsteps) load_scal((it_begin + j + 3) * kTile);
-    const bool act = active(j);
-    const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int i0 = (it_begin + j) * kTile;
-    f32x16 sx = zero16(), gx = zero16(), px = zero16(), hx = zero16();
-    if (act) {
-      if constexpr (!PIPE) {
-        sc = zero16();
-        gc = zero16();
-        pc = zero16();
-        hc = zero16();
+    if (active(j)) {
+      sc = zero16();
+      gc = zero16();
+      pc = zero16();
+      hc = zero16();
 #pragma unroll
-        for (int t = 0; t < DK; ++t) scores_kstep(S, t, sc, gc, pc, hc);
-      }
+      for (int t = 0; t < DK; ++t) scores_kstep(S, t, sc, gc, pc, hc);
       // Row scalars of the streamed queries: lane group g holds rows kappa(r, g), which
       // for r = 4 r4 .. 4 r4 + 3 are the 4 consecutive rows 8 r4 + 4 g .. + 3.
       const float* sv = scal(S);
@@ -335,11 +324,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
         vset<TT>(wdp[kk], ss, p * (gv - al));
       };
 #pragma unroll
-      for (int t = 0; t < DK; ++t) {
-        if constexpr (PIPE) scores_kstep(SN, t, sx, gx, px, hx);  // stale (unused) on the last step
+      for (int t = 0; t < DK; ++t)
 #pragma unroll
         for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
-      }
 #pragma unroll
       for (int t = 0; t < NK; ++t)
 #pragma unroll
@@ -355,15 +342,6 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass2_kernel(Pass2Args a) {
           accK[mb] = TT::mfma(tq, wsb[t], accK[mb]);
           accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);
         }
-    } else if (PIPE && act_next) {
-#pragma unroll
-      for (int t = 0; t < DK; ++t) scores_kstep(SN, t, sx, gx, px, hx);
-    }
-    if constexpr (PIPE) {
-      sc = sx;
-      gc = gx;
-      pc = px;
-      hc = hx;
     }
     wait_vmem();
     __syncthreads();

@@ -79,6 +79,8 @@ hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s)
 // (alpha known), sweep 2 gQ and gdO (alpha and E known); each with its split merge.
 hipError_t launch_fourpass_sweep(const Pass1Args& a, int sweep, DT dt, int d, bool causal, hipStream_t s);
 __host__ __device__ inline size_t fourpass_record_floats(int d) { return (size_t)2 * (d / 32) * 16 * 64; }
+// 16-bit pass 2 at d = 64 is built for two waves per SIMD (two workgroups per CU).
+inline int pass2_blocks_per_cu(DT dt, int d) { return (dt != DT::F32 && d == 64) ? 2 : 1; }
 hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
 hipError_t launch_pass2_reduce(const Pass2Args& a, DT dt, int d, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& a, DT dt, int d, int BH, hipStream_t s);
