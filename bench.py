@@ -119,21 +119,33 @@ def digest_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
     print(json.dumps(summary, indent=1))
 
 
-def digest_trace(trace_dir, out):
+def digest_trace(trace_dir, out, bench_log=None):
     rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    traced = None
+    if bench_log:
+        with open(bench_log) as fh:
+            for line in fh:
+                if line.startswith("{") and '"roofline"' in line:
+                    traced = json.loads(line)
     lines = ["# Kernel trace: BoB call at long_16k (B=1, H=1, N=16384, d=64, bf16, non-causal)", "",
              "Commands (repository root, one MI355X):", "", "```",
              "rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py --steps 5 "
-             "--warmup 2 --no-cpu --no-endpoint --no-parity",
-             "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT), "```", "",
+             "--warmup 2 --no-cpu --no-endpoint --no-parity --no-breakdown > <TRACED_STDOUT>",
+             "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT) + " <TRACED_STDOUT>", "```", "",
              f"Pass-1 source hash ({' + '.join(PASS1_SOURCES)}): {pass1_source_hash()}", "",
              "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
     for r in rows:
         n = r["Name"].replace("void fb::", "").split("(")[0]
         lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    lines += ["", "Calls include bench.py's 2 warm-up steps and its 5 untimed repeats (for the call time without "
-              "per-kernel events)."]
+    lines += ["", "Calls: bench.py's 2 warm-up calls, its 5 timed calls (HIP events around pass 1 only) and 5 "
+              "repeats without any library events."]
+    if traced:
+        r = traced["roofline"]
+        lines += ["", f"The traced bench.py run itself reported {traced['ms_per_step'] * 1e3:.1f} us per call and "
+                  f"{r['avg_launch_ms'] * 1e3:.1f} us per `{r['kernel']}` launch (HIP events, timed region). Under "
+                  "the profiler every kernel runs slower than in an untraced bench.py run, whose figures are the "
+                  "ones reported."]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -240,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-endpoint", action="store_true", help="skip the N=262144 feasibility call")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the untimed pass with HIP events around every kernel (the kernels field is then empty)")
     ap.add_argument("--hutchinson", action="store_true",
                     help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
     ap.add_argument("--schedule", choices=("two_pass", "four_pass"), default="two_pass",
@@ -248,7 +262,7 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (csv dirs) into OUT (json)")
-    ap.add_argument("--digest-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
+    ap.add_argument("--digest-trace", nargs="+", metavar="TRACE_DIR OUT [BENCH_LOG]",
                     help="summarise a rocprofv3 --kernel-trace --stats run (csv dir) into OUT (markdown)")
     args = ap.parse_args()
     if args.digest_pmc:
@@ -309,11 +323,13 @@ def main():
     dom, dom_units = ("bob_pass1", UNITS["pass1"]) if args.schedule == "two_pass" else ("fourpass_rows", 9)
 
     # per-kernel breakdown (untimed): HIP events around every launch of the library
-    fb.profile_start()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kernels = fb.profile_stop()
+    kernels = {}
+    if not args.no_breakdown:
+        fb.profile_start()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        kernels = fb.profile_stop()
 
     # timed region: whole-call time with stream events; the library records HIP events
     # around the dominant kernel only, on its launch stream, for the roofline
