@@ -118,12 +118,13 @@ def test_bob_splits_fp32_tight():
     _check_full(workload.custom(1, 1, 700, 64, "fp32", True), splits=(3, 4))
 
 
-@pytest.mark.parametrize("tau", [0.3, -0.125, 0.0])
+@pytest.mark.parametrize("tau", [0.3, -0.125, 0.0, 0.25])
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, False), ("bf16", 64, True), ("bf16", 128, True),
                                             ("fp32", 64, True)])
 def test_bob_any_tau(tau, dtype, d, causal):
-    """Any finite scale: not a power of two, negative, and zero (uniform softmax; the
-    exact gQ and gK are then zero and are measured on the scale of gV and gdO)."""
+    """Any finite scale: not a power of two, negative, zero (uniform softmax; the exact
+    gQ and gK are then zero and are measured on the scale of gV and gdO), and a power of
+    two other than the default."""
     _check_full(workload.custom(1, 2, 300, d, dtype, causal, tau=tau))
 
 
