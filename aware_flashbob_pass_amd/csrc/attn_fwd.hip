@@ -53,11 +53,13 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
   }
 }
 
-// Pipelined variant for 16-bit inputs (same staging scheme as pass 1): K and V
-// tiles in three row-major LDS stages prefetched two steps ahead; the next
-// step's score tile is formed while the current one goes through the online
-// softmax; P V reads V^T operands with the transposing LDS load. The running
-// rescale of the accumulators is skipped when no row maximum of the wave grew.
+// Staged variant for 16-bit inputs (same staging scheme as pass 1): K and V
+// tiles in three row-major LDS stages loaded two steps ahead; each step forms
+// its score tile, runs the online softmax and accumulates P V, reading V^T
+// operands with the transposing LDS load. At d = 64 three to four waves share
+// each SIMD, which hides more than forming the next step's tile early did. The
+// running rescale of the accumulators is skipped when no row maximum of the wave
+// grew.
 // With `nsplit` > 1 each split covers a key range and writes a record
 // (accumulators, max, partial denominators) that fwd_combine merges.
 template <class TT, int D, bool CAUSAL, bool WITH_D>
@@ -109,20 +111,16 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(Fwd
   wait_vmem();
   __syncthreads();
 
-  f32x16 sc = zero16();
-  if (nsteps > 0 && active(0)) {
-#pragma unroll
-    for (int t = 0; t < DK; ++t) sc = TT::mfma(lds_row_op<TT, D>(stage(0, 0), n, t, g), bq[t], sc);
-  }
+  f32x16 sc;  // score tile of the current step
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
-    constexpr int SN = (S + 1) % NBUF, SC = (S + 2) % NBUF;
+    constexpr int SC = (S + 2) % NBUF;
     if (j + 2 < nsteps) issue(SC, j + 2);  // buffer SC was last read in step j - 1
-    const bool act = active(j);
-    const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int k0 = (kt_begin + j) * kTile;
-    f32x16 sx = zero16();
-    if (act) {
+    if (active(j)) {
+      sc = zero16();
+#pragma unroll
+      for (int t = 0; t < DK; ++t) sc = TT::mfma(lds_row_op<TT, D>(stage(S, 0), n, t, g), bq[t], sc);
       // With cs > 0 the scale stays folded into the exponent (p = 2^(raw cs - m)): the
       // maximum of the raw scores times cs equals the maximum of the scaled scores
       // (rounding is monotonic) and masked raw scores of -inf still give p = 0. With
@@ -152,7 +150,6 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(Fwd
       V pp[NK];
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
-        sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);  // stale on the last step
 #pragma unroll
         for (int r = t * 16 / DK; r < (t + 1) * 16 / DK; ++r) {
           const float p = fast_exp2(fmaf(sc[r], cm, -m));
@@ -164,11 +161,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(Fwd
       for (int t = 0; t < NK; ++t)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] = TT::mfma(lds_tr_op<TT, D>(stage(S, 1), mb, t, lane), pp[t], acc[mb]);
-    } else if (act_next) {
-#pragma unroll
-      for (int t = 0; t < DK; ++t) sx = TT::mfma(lds_row_op<TT, D>(stage(SN, 0), n, t, g), bq[t], sx);
     }
-    sc = sx;
     wait_vmem();
     __syncthreads();
   };
