@@ -410,23 +410,52 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   st = check_no_alias({{"dQ", dQ}, {"dK", dK}, {"dV", dV}, {"D_out", D_out}},
                       {{"Q", Q}, {"K", K}, {"V", V}, {"O", O}, {"dO", dO}, {"L", L}});
   if (st) return st;
-  float* D = D_out;
-  void* tmp = nullptr;
-  if (!D) {
-    const size_t bytes = (size_t)B * H * N * sizeof(float);
-    hipError_t e = hipMallocAsync(&tmp, bytes, stream);
-    if (e != hipSuccess || !tmp) {
-      (void)hipGetLastError();
-      return fail(FB_ERR_OOM, "scratch allocation of %zu bytes failed", bytes);
-    }
-    D = static_cast<float*>(tmp);
-  }
   const DT dt = to_dt(dtype);
   const int BH = B * H;
+  // 16-bit inputs run the staged kernels, which may split the streamed range and
+  // then need record buffers; float32 runs the single-buffered kernels.
+  int s0 = 1, s1 = 1, s2 = 1;
+  size_t rec_bytes = 0;
+  if (dt != DT::F32) {
+    splits_for(BH, N, dt, d, &s0, &s1, &s2);
+    const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
+    const size_t r1 = s1 > 1 ? (size_t)s1 * tiles * fb::first_bwd_dq_record_floats(d) * sizeof(float) : 0;
+    const size_t r2 = s2 > 1 ? (size_t)s2 * tiles * fb::pass2_record_floats(d) * sizeof(float) : 0;
+    rec_bytes = align256(std::max(r1, r2));  // dQ's records are merged before dK/dV writes its own
+  }
+  const size_t d_bytes = D_out ? 0 : align256((size_t)BH * N * sizeof(float));
+  void* tmp = nullptr;
+  if (d_bytes + rec_bytes) {
+    hipError_t e = hipMallocAsync(&tmp, d_bytes + rec_bytes, stream);
+    if (e != hipSuccess || !tmp) {
+      (void)hipGetLastError();
+      return fail(FB_ERR_OOM, "scratch allocation of %zu bytes failed", d_bytes + rec_bytes);
+    }
+  }
+  float* D = D_out ? D_out : static_cast<float*>(tmp);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(tmp) + d_bytes);
   fb::BwdArgs ba{Q, K, V, O, dO, L, D, dQ, dK, dV, tau, N};
   st = run("attn_bwd_rowdot", stream, [&] { return fb::launch_bwd_rowdot(ba, dt, d, BH, stream); });
-  if (!st) st = run("attn_bwd_dq", stream, [&] { return fb::launch_bwd_dq(ba, dt, d, causal != 0, BH, stream); });
-  if (!st) st = run("attn_bwd_dkdv", stream, [&] { return fb::launch_bwd_dkdv(ba, dt, d, causal != 0, BH, stream); });
+  if (dt == DT::F32) {
+    if (!st) st = run("attn_bwd_dq", stream, [&] { return fb::launch_bwd_dq(ba, dt, d, causal != 0, BH, stream); });
+    if (!st)
+      st = run("attn_bwd_dkdv", stream, [&] { return fb::launch_bwd_dkdv(ba, dt, d, causal != 0, BH, stream); });
+  } else {
+    // the tensors the first backward does not read (UQ, UK, UV) point at valid inputs
+    fb::Pass1Args p1{};
+    p1.Q = Q; p1.K = K; p1.V = V; p1.dO = dO; p1.UQ = Q; p1.UK = K; p1.UV = V; p1.O = O;
+    p1.L = L; p1.D = D; p1.gQ = dQ; p1.part = part;
+    p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = s1;
+    if (!st) st = run("attn_bwd_dq", stream, [&] { return fb::launch_first_bwd_dq(p1, dt, d, causal != 0, stream); });
+    fb::Pass2Args p2{};
+    p2.Q = Q; p2.K = K; p2.V = V; p2.dO = dO; p2.UQ = Q; p2.UK = K; p2.UV = V;
+    p2.L = L; p2.D = D; p2.gK = dK; p2.gV = dV; p2.part = part;
+    p2.tau = tau; p2.N = N; p2.BH = BH; p2.nsplit = s2;
+    if (!st)
+      st = run("attn_bwd_dkdv", stream, [&] { return fb::launch_first_bwd_dkdv(p2, dt, d, causal != 0, stream); });
+    if (!st && s2 > 1)
+      st = run("attn_bwd_dkdv_reduce", stream, [&] { return fb::launch_pass2_reduce(p2, dt, d, stream); });
+  }
   if (tmp) {
     std::string msg = g_err;
     hipError_t ef = hipFreeAsync(tmp, stream);

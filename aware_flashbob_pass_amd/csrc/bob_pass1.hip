@@ -158,13 +158,18 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
 }
 
 // ---- four-pass ablation schedule (modes of the pipelined kernel) -----------------
-enum : int { kTwoPass = 0, kAlphaPass = 1, kEnergyPass = 2, kRowsPass = 3 };
+enum : int { kTwoPass = 0, kAlphaPass = 1, kEnergyPass = 2, kRowsPass = 3, kDqPass = 4 };
+// kDqPass is not part of BoB: it is the query-side half of the first backward g
+// (dQ = tau dS K with dS = P (dP - D)), run by the same staged sweep so that the
+// autograd path's first backward uses the same kernels as the rest.
 
 // Record of one wave: the row partial (alpha or E sweeps) or the two row-output
 // accumulators (rows sweep), lane-contiguous.
 template <class TT, int D, int MODE>
 __device__ inline float* fourpass_record(const Pass1Args& a, int split, int bh, int qt, int wave) {
-  constexpr size_t REC = MODE == kRowsPass ? (size_t)2 * (D / 32) * 16 * 64 : 64;
+  constexpr size_t REC = MODE == kRowsPass ? (size_t)2 * (D / 32) * 16 * 64
+                         : MODE == kDqPass  ? (size_t)(D / 32) * 16 * 64
+                                            : 64;
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave;
   return a.part + rec * REC;
 }
@@ -180,6 +185,17 @@ __device__ inline void fourpass_epilogue(const f32x16 (&Q)[D / 32], const f32x16
     if (g == 0) a.alpha[row] = total;
   } else if constexpr (MODE == kEnergyPass) {
     if (g == 0) a.E[row] = total;
+  } else if constexpr (MODE == kDqPass) {
+    T* dQ = reinterpret_cast<T*>(a.gQ) + row * D;
+    const float tau = a.tau;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = mb * 32 + kappa(r4 * 4, g);
+        const int r = r4 * 4;
+        store4<TT>(dQ + dim, tau * Q[mb][r], tau * Q[mb][r + 1], tau * Q[mb][r + 2], tau * Q[mb][r + 3]);
+      }
   } else {
     T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
     T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
@@ -200,7 +216,10 @@ template <class TT, int D, int MODE>
 __device__ inline void fourpass_write_record(const f32x16 (&Q)[D / 32], const f32x16 (&X)[D / 32], float s_p,
                                              int split, int bh, int qt, int wave, int lane, const Pass1Args& a) {
   float* R = fourpass_record<TT, D, MODE>(a, split, bh, qt, wave);
-  if constexpr (MODE == kRowsPass) {
+  if constexpr (MODE == kDqPass) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) store_acc16(R + (mb * 64 + lane) * 16, Q[mb]);
+  } else if constexpr (MODE == kRowsPass) {
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       store_acc16(R + ((0 * (D / 32) + mb) * 64 + lane) * 16, Q[mb]);
@@ -227,7 +246,10 @@ __global__ __launch_bounds__(kBlock) void fourpass_combine_kernel(Pass1Args a) {
   float s_p = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) {
     const float* R = fourpass_record<TT, D, MODE>(a, sp, bh, blockIdx.x, wave);
-    if constexpr (MODE == kRowsPass) {
+    if constexpr (MODE == kDqPass) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) Q[mb] += load_acc16(R + (mb * 64 + lane) * 16);
+    } else if constexpr (MODE == kRowsPass) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         Q[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
@@ -295,6 +317,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   constexpr bool PIPE = D == 64;
   constexpr bool TWO = MODE == kTwoPass;
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
+  constexpr bool NEED_G = MODE != kDqPass;      // the first backward needs S and dP only
+  constexpr bool NEED_H = NEED_DP && NEED_G;
   constexpr int NH = TWO ? P1<TT, D>::NH : 1;
   constexpr int MBA = TWO ? P1<TT, D>::MBA : MB;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
@@ -315,7 +339,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   V bq[DK], bdo[DK], buq[DK];
   load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
   load_resident<TT, D>(reinterpret_cast<const T*>(a.dO) + base, qi, N, g, bdo);
-  load_resident<TT, D>(reinterpret_cast<const T*>(a.UQ) + base, qi, N, g, buq);
+  if constexpr (NEED_G) load_resident<TT, D>(reinterpret_cast<const T*>(a.UQ) + base, qi, N, g, buq);
   const size_t rowv = (size_t)bh * N + (qi < N ? qi : 0);
   const float lq = a.L[rowv] * kLog2e;
   const float dq = a.D[rowv];
@@ -343,11 +367,14 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
   auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
 
+  // tiles a mode reads: K always, V for dP, UK for G, UV for H
+  constexpr bool NEED_TILE[NT] = {true, NEED_DP, NEED_G, NEED_H};
   auto issue = [&](int stg, int j) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS, wave,
-                                        lane);
+      if (NEED_TILE[t])
+        stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS,
+                                          wave, lane);
   };
   for (int j = 0; j < 2 && j < nsteps; ++j) issue(j, j);
   wait_vmem();
@@ -363,12 +390,12 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
       const V auk = lds_row_op<TT, D>(stage(0, 2), n, t, g);
       const V auv = lds_row_op<TT, D>(stage(0, 3), n, t, g);
       sc = TT::mfma(ak, bq[t], sc);
-      gc = TT::mfma(ak, buq[t], gc);
-      gc = TT::mfma(auk, bq[t], gc);
-      if constexpr (NEED_DP) {
-        pc = TT::mfma(av, bdo[t], pc);
-        hc = TT::mfma(auv, bdo[t], hc);
+      if constexpr (NEED_G) {
+        gc = TT::mfma(ak, buq[t], gc);
+        gc = TT::mfma(auk, bq[t], gc);
       }
+      if constexpr (NEED_DP) pc = TT::mfma(av, bdo[t], pc);
+      if constexpr (NEED_H) hc = TT::mfma(auv, bdo[t], hc);
     }
   }
 
@@ -404,12 +431,12 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           const V auk = lds_row_op<TT, D>(cuk, n, t, g);
           const V auv = lds_row_op<TT, D>(cuv, n, t, g);
           sc = TT::mfma(ak, bq[t], sc);
-          gc = TT::mfma(ak, buq[t], gc);
-          gc = TT::mfma(auk, bq[t], gc);
-          if constexpr (NEED_DP) {
-            pc = TT::mfma(av, bdo[t], pc);
-            hc = TT::mfma(auv, bdo[t], hc);
+          if constexpr (NEED_G) {
+            gc = TT::mfma(ak, buq[t], gc);
+            gc = TT::mfma(auk, bq[t], gc);
           }
+          if constexpr (NEED_DP) pc = TT::mfma(av, bdo[t], pc);
+          if constexpr (NEED_H) hc = TT::mfma(auv, bdo[t], hc);
         }
       }
       // log2-domain scores, masked where the key is out of range or after the query
@@ -432,6 +459,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         } else if constexpr (MODE == kEnergyPass) {
           const float dpv = pc[r];
           e0_p += p * (fmaf(gv, dpv - dq, hc[r]) - al * dpv);  // P Pbar: E directly
+        } else if constexpr (MODE == kDqPass) {
+          vset<TT>(wa[kk], ss, p * (pc[r] - dq));  // dS
         } else if constexpr (MODE == kRowsPass) {
           const float dpv = pc[r];
           const float t1 = dpv - dq;
@@ -471,10 +500,10 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           if (t + 1 < DK) fetch_row(t + 1, ro[(t + 1) & 1]);
           const V(&o)[4] = ro[t & 1];
           sx = TT::mfma(o[0], bq[t], sx);
-          gx = TT::mfma(o[0], buq[t], gx);
+          if constexpr (NEED_G) gx = TT::mfma(o[0], buq[t], gx);
           if constexpr (NEED_DP) px = TT::mfma(o[1], bdo[t], px);
-          gx = TT::mfma(o[2], bq[t], gx);
-          if constexpr (NEED_DP) hx = TT::mfma(o[3], bdo[t], hx);
+          if constexpr (NEED_G) gx = TT::mfma(o[2], bq[t], gx);
+          if constexpr (NEED_H) hx = TT::mfma(o[3], bdo[t], hx);
 #pragma unroll
           for (int r = t * 8 / DK; r < (t + 1) * 8 / DK; ++r) elementwise(r);
         }
@@ -511,7 +540,9 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           for (int r = 8 + mb * 8 / MBA; r < 8 + (mb + 1) * 8 / MBA; ++r) elementwise(r);
         }
         const V(&o)[4] = to[q & 1];
-        if constexpr (MODE == kRowsPass) {
+        if constexpr (MODE == kDqPass) {
+          accA[mb] = TT::mfma(o[0], wa[t], accA[mb]);  // dS K
+        } else if constexpr (MODE == kRowsPass) {
           accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);  // dS UK
           accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);  // P UV
           accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);  // Sbar K
@@ -535,12 +566,12 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
         const V auk = lds_row_op<TT, D>(nuk, n, t, g);
         const V auv = lds_row_op<TT, D>(nuv, n, t, g);
         sx = TT::mfma(ak, bq[t], sx);
-        gx = TT::mfma(ak, buq[t], gx);
-        gx = TT::mfma(auk, bq[t], gx);
-        if constexpr (NEED_DP) {
-          px = TT::mfma(av, bdo[t], px);
-          hx = TT::mfma(auv, bdo[t], hx);
+        if constexpr (NEED_G) {
+          gx = TT::mfma(ak, buq[t], gx);
+          gx = TT::mfma(auk, bq[t], gx);
         }
+        if constexpr (NEED_DP) px = TT::mfma(av, bdo[t], px);
+        if constexpr (NEED_H) hx = TT::mfma(auv, bdo[t], hx);
       }
     }
     if constexpr (PIPE) {
@@ -690,6 +721,14 @@ static hipError_t launch_fp_tt(const Pass1Args& a, int sweep, int d, bool causal
     case 0: return launch_fp_m<TT, kAlphaPass>(a, d, causal, s);
     case 1: return launch_fp_m<TT, kEnergyPass>(a, d, causal, s);
     default: return launch_fp_m<TT, kRowsPass>(a, d, causal, s);
+  }
+}
+
+hipError_t launch_first_bwd_dq(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return launch_fp_m<BF16, kDqPass>(a, d, causal, s);
+    case DT::F16: return launch_fp_m<F16, kDqPass>(a, d, causal, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
 // 256 registers, so two waves share each SIMD (two workgroups per CU) and each
 // one's matrix-core work overlaps the other's vector work; that beat forming
 // the next step's tiles during the current step at one wave per SIMD.
-template <class TT, int D, bool CAUSAL>
+template <class TT, int D, bool CAUSAL, bool FIRST = false>
 __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pass2Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
@@ -205,15 +205,21 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   const size_t vbase = (size_t)bh * N;
   const T* src[NT] = {reinterpret_cast<const T*>(a.Q) + base, reinterpret_cast<const T*>(a.dO) + base,
                       reinterpret_cast<const T*>(a.UQ) + base};
-  const float* vsrc[4] = {a.L + vbase, a.D + vbase, a.alpha + vbase, a.E + vbase};
+  // FIRST (the first backward g: dK = tau dS^T Q, dV = P^T dO) needs S and dP only:
+  // no UQ tile, no UK / UV rows, and only the L and D row scalars.
+  constexpr int NSCAL = FIRST ? 2 : 4;
+  const float* vsrc[4] = {a.L + vbase, a.D + vbase, FIRST ? nullptr : a.alpha + vbase,
+                          FIRST ? nullptr : a.E + vbase};
   const int k0w = kt * kBlockRows + wave * kTile;
   const int kj = k0w + n;
 
   V bk[DK], bv[DK], buk[DK], buv[DK];
   load_resident<TT, D>(reinterpret_cast<const T*>(a.K) + base, kj, N, g, bk);
   load_resident<TT, D>(reinterpret_cast<const T*>(a.V) + base, kj, N, g, bv);
-  load_resident<TT, D>(reinterpret_cast<const T*>(a.UK) + base, kj, N, g, buk);
-  load_resident<TT, D>(reinterpret_cast<const T*>(a.UV) + base, kj, N, g, buv);
+  if constexpr (!FIRST) {
+    load_resident<TT, D>(reinterpret_cast<const T*>(a.UK) + base, kj, N, g, buk);
+    load_resident<TT, D>(reinterpret_cast<const T*>(a.UV) + base, kj, N, g, buv);
+  }
   const float cs = a.tau * kLog2e;
   const float tau = a.tau;
 
@@ -238,18 +244,18 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   float sreg = 0.f;  // one of the 4 x 32 row scalars of a later stage (threads 0..127)
   auto load_scal = [&](int i0) {
     sreg = 0.f;
-    if (tid < 4 * kTile) {
+    if (tid < NSCAL * kTile) {
       const int which = tid / kTile, row = i0 + tid % kTile;
       if (row < N) sreg = vsrc[which][row] * (which == 0 ? kLog2e : 1.f);
     }
   };
   auto put_scal = [&](int stg) {
-    if (tid < 4 * kTile) scal(stg)[tid] = sreg;
+    if (tid < NSCAL * kTile) scal(stg)[tid] = sreg;
   };
   auto issue = [&](int stg, int j) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      stage_direct<TT, D, kBlock / 64>(src[t], (it_begin + j) * kTile, N, tile(stg, t), wave, lane);
+      if (!FIRST || t < 2) stage_direct<TT, D, kBlock / 64>(src[t], (it_begin + j) * kTile, N, tile(stg, t), wave, lane);
   };
   for (int j = 0; j < 2 && j < nsteps; ++j) {
     issue(j, j);
@@ -266,10 +272,12 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
     const V ado = lds_row_op<TT, D>(tile(j, 1), n, t, g);
     const V auq = lds_row_op<TT, D>(tile(j, 2), n, t, g);
     s_ = TT::mfma(aq, bk[t], s_);
-    g_ = TT::mfma(auq, bk[t], g_);
-    g_ = TT::mfma(aq, buk[t], g_);
+    if constexpr (!FIRST) {
+      g_ = TT::mfma(auq, bk[t], g_);
+      g_ = TT::mfma(aq, buk[t], g_);
+    }
     p_ = TT::mfma(ado, bv[t], p_);
-    h_ = TT::mfma(ado, buv[t], h_);
+    if constexpr (!FIRST) h_ = TT::mfma(ado, buv[t], h_);
   };
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
@@ -310,18 +318,25 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
       auto elementwise = [&](int r) {
         if ((r & 3) == 0) {
           d4 = row4(1, r >> 2);
-          a4 = row4(2, r >> 2);
-          e4 = row4(3, r >> 2);
+          if constexpr (!FIRST) {
+            a4 = row4(2, r >> 2);
+            e4 = row4(3, r >> 2);
+          }
         }
-        const float dq = d4[r & 3], al = a4[r & 3], eq = e4[r & 3];
+        const float dq = d4[r & 3];
         const float p = fast_exp2(sc[r]);
-        const float gv = gc[r] * tau;
         const float dpv = pc[r];
         const float t1 = dpv - dq;
         const int kk = r >> 3, ss = r & 7;
-        vset<TT>(wds[kk], ss, p * t1);
-        vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(al, dpv, eq)));
-        vset<TT>(wdp[kk], ss, p * (gv - al));
+        vset<TT>(wds[kk], ss, p * t1);  // dS
+        if constexpr (FIRST) {
+          vset<TT>(wdp[kk], ss, p);  // P
+        } else {
+          const float al = a4[r & 3], eq = e4[r & 3];
+          const float gv = gc[r] * tau;
+          vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(al, dpv, eq)));  // Sbar
+          vset<TT>(wdp[kk], ss, p * (gv - al));                                  // dPbar
+        }
       };
 #pragma unroll
       for (int t = 0; t < DK; ++t)
@@ -338,9 +353,13 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
 #pragma unroll
             for (int r = 8 + mb * 8 / MB; r < 8 + (mb + 1) * 8 / MB; ++r) elementwise(r);
           }
-          accK[mb] = TT::mfma(tuq, wds[t], accK[mb]);
-          accK[mb] = TT::mfma(tq, wsb[t], accK[mb]);
-          accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);
+          if constexpr (FIRST) {
+            accK[mb] = TT::mfma(tq, wds[t], accK[mb]);  // dS^T Q
+          } else {
+            accK[mb] = TT::mfma(tuq, wds[t], accK[mb]);  // dS^T UQ
+            accK[mb] = TT::mfma(tq, wsb[t], accK[mb]);   // Sbar^T Q
+          }
+          accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);    // P^T dO or dPbar^T dO
         }
     }
     wait_vmem();
@@ -420,6 +439,30 @@ template <class TT>
 static hipError_t launch_p2_tt(const Pass2Args& a, int d, bool causal, hipStream_t s) {
   if (d == 64) return causal ? launch_p2_t<TT, 64, true>(a, s) : launch_p2_t<TT, 64, false>(a, s);
   return causal ? launch_p2_t<TT, 128, true>(a, s) : launch_p2_t<TT, 128, false>(a, s);
+}
+
+template <class TT, int D, bool CAUSAL>
+static hipError_t launch_fb_dkdv_t(const Pass2Args& a, hipStream_t s) {
+  const size_t lds = pass2_lds_bytes<TT, D>();
+  hipError_t e = ensure_lds(&bob_pass2_kernel<TT, D, CAUSAL, true>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bob_pass2_kernel<TT, D, CAUSAL, true>), dim3(row_tiles(a.N), a.BH, a.nsplit), dim3(kBlock), lds,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <class TT>
+static hipError_t launch_fb_dkdv_tt(const Pass2Args& a, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? launch_fb_dkdv_t<TT, 64, true>(a, s) : launch_fb_dkdv_t<TT, 64, false>(a, s);
+  return causal ? launch_fb_dkdv_t<TT, 128, true>(a, s) : launch_fb_dkdv_t<TT, 128, false>(a, s);
+}
+
+hipError_t launch_first_bwd_dkdv(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s) {
+  switch (dt) {
+    case DT::BF16: return launch_fb_dkdv_tt<BF16>(a, d, causal, s);
+    case DT::F16: return launch_fb_dkdv_tt<F16>(a, d, causal, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s) {

@@ -78,6 +78,12 @@ hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s)
 // Four-pass ablation schedule, 16-bit inputs: sweep 0 writes alpha, sweep 1 E
 // (alpha known), sweep 2 gQ and gdO (alpha and E known); each with its split merge.
 hipError_t launch_fourpass_sweep(const Pass1Args& a, int sweep, DT dt, int d, bool causal, hipStream_t s);
+// First backward on the staged 16-bit kernels (with its split merge when nsplit > 1):
+// dQ = tau dS K written to a.gQ (reads Q, K, V, dO, L, D), and dK = tau dS^T Q,
+// dV = P^T dO written to a.gK, a.gV (reads Q, K, V, dO, L, D).
+hipError_t launch_first_bwd_dq(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s);
+hipError_t launch_first_bwd_dkdv(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
+__host__ __device__ inline size_t first_bwd_dq_record_floats(int d) { return (size_t)(d / 32) * 16 * 64; }
 __host__ __device__ inline size_t fourpass_record_floats(int d) { return (size_t)2 * (d / 32) * 16 * 64; }
 // 16-bit pass 2 at d = 64 is built for two waves per SIMD (two workgroups per CU).
 inline int pass2_blocks_per_cu(DT dt, int d) { return (dt != DT::F32 && d == 64) ? 2 : 1; }

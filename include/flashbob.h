@@ -149,8 +149,12 @@ fb_status_t attn_fwd(const void* Q, const void* K, const void* V, const void* dO
  * attn_bwd: the first backward g (the map BoB differentiates).
  * In: Q, K, V, O, dO [B][H][N][d] dtype; L [B][H][N] float32 from attn_fwd.
  * Out: dQ, dK, dV [B][H][N][d] dtype; D_out optional [B][H][N] float32
- * (rowsum(dO * O)). Allocates a B*H*N float32 scratch vector with
- * hipMallocAsync when D_out is NULL.
+ * (rowsum(dO * O)). Scratch (a B*H*N float32 vector when D_out is NULL, and for
+ * bf16/fp16 inputs the partial sums of a split streamed range, sized like
+ * bob_workspace_bytes' split records) is allocated with hipMallocAsync and freed
+ * with hipFreeAsync on `stream`; FB_ERR_OOM if that fails. bf16/fp16 inputs run
+ * the staged kernels of pass 1 and pass 2 restricted to S and dP; float32 inputs
+ * run single-buffered kernels.
  */
 fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* L, float tau, int causal, int B, int H, int N, int d,

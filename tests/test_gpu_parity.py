@@ -202,6 +202,28 @@ def test_attn_bwd(dtype, d, causal):
         assert rel(to_f64(got.cpu()), exp) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("splits", [(1, 1), (3, 5)])
+def test_attn_bwd_staged_splits(dtype, d, causal, splits):
+    """The 16-bit first backward (staged kernels) with and without a split streamed range."""
+    fb = _fb()
+    w = workload.custom(1, 2, 1000, d, dtype, causal)
+    cpu, g = _gpu_inputs(w, 9)
+    _note(f"attn_bwd {w.describe()} splits={splits}")
+    o, lse = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=causal)
+    fb.set_tuning(*splits)
+    try:
+        dq, dk, dv, dvec = fb.attn_bwd(g["Q"], g["K"], g["V"], o, g["dO"], lse, tau=w.scale, causal=causal)
+        torch.cuda.synchronize()
+    finally:
+        fb.set_tuning(0, 0)
+    ref = oracle.first_backward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), to_f64(cpu["dO"]),
+                                w.scale, causal)
+    for got, exp in zip((dq, dk, dv, dvec), ref):
+        assert rel(to_f64(got.cpu()), exp) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_with_stats_row_scalars(dtype):
     """alpha and E (the two row scalars that cross the pass boundary) against the oracle's."""
