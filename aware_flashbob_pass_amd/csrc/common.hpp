@@ -194,44 +194,6 @@ __device__ inline void load_resident(const typename TT::elem* __restrict__ src, 
   }
 }
 
-// ---- pipelined staging (16-bit types) -------------------------------------------
-// One stage = 32 streamed rows of NT [N][D] tensors, copied global -> registers
-// (load) one step ahead of use and registers -> row-major padded LDS (commit).
-template <class TT, int D, int NT, int NTHREADS>
-struct StagePrefetch {
-  using T = typename TT::elem;
-  static constexpr int CH = 16 / sizeof(T);
-  static constexpr int CPR = D / CH;
-  static constexpr int NCH = kTile * CPR;
-  static constexpr int PER = (NCH + NTHREADS - 1) / NTHREADS;
-  uint4 r[NT][PER];
-
-  __device__ inline void load(const T* const (&src)[NT], int r0, int N, int tid) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int c = tid + p * NTHREADS;
-        const int row = c / CPR, e0 = (c % CPR) * CH;
-        const int grow = r0 + row;
-        r[t][p] = make_uint4(0u, 0u, 0u, 0u);
-        if (c < NCH && grow < N) r[t][p] = *reinterpret_cast<const uint4*>(src[t] + (size_t)grow * D + e0);
-      }
-  }
-  __device__ inline void commit(T* const (&dst)[NT], int tid) const {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int c = tid + p * NTHREADS;
-        if (c < NCH) {
-          const int row = c / CPR, e0 = (c % CPR) * CH;
-          *reinterpret_cast<uint4*>(dst[t] + roff<TT, D>(row, e0)) = r[t][p];
-        }
-      }
-  }
-};
-
 // Direct global -> LDS staging of one 32-row stage of a [N][D] tensor (16-bit
 // types): each wave issues global_load_lds_dwordx4, whose lane L writes the 16
 // bytes at (wave-uniform LDS base) + 16 L. LDS slot s of the tile is row
