@@ -8,9 +8,9 @@
 // H = dO UV^T, dP = dO V^T, P = exp(tau Q K^T - L)):
 //   alpha_i = sum_j P G,                   E_i = sum_j W_b - alpha_i D_i,
 //   W_a = P (dP - D),  W_b = P (G (dP - D) + H),
-//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i (P dP) K - E_i P K ],
+//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i W_a K - e0_i P K ],  e0_i = sum_j W_b,
 //   gdO_i = (P UV + (P G) V) - alpha_i O_i.
-// The six alpha-free contractions W_a UK, W_b K, (P dP) K, P K, P UV and
+// The six alpha-free contractions W_a UK, W_b K, W_a K, P K, P UV and
 // (P G) V accumulate into four float32 register tiles (A, B, C, X below); the
 // pages name six alpha-free accumulators without listing them, and this is our
 // reading of them.
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
     }
 
     // element-wise weights
-    V wa[G::NK], wb[G::NK], pd[G::NK], pp[G::NK], pg[G::NK];
+    V wa[G::NK], wb[G::NK], pp[G::NK], pg[G::NK];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + kappa(r, g);
@@ -125,7 +125,6 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
       const int kk = r / TT::KPL, ss = r % TT::KPL;
       vset<TT>(wa[kk], ss, p * t1);
       vset<TT>(wb[kk], ss, vwb);
-      vset<TT>(pd[kk], ss, p * dpv);
       vset<TT>(pp[kk], ss, p);
       vset<TT>(pg[kk], ss, vpg);
     }
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
         const V tuv = lds_t_op<TT, D>(uv_t, dim, t, g);
         accA[mb] = TT::mfma(tuk, wa[t], accA[mb]);
         accA[mb] = TT::mfma(tk, wb[t], accA[mb]);
-        accB[mb] = TT::mfma(tk, pd[t], accB[mb]);
+        accB[mb] = TT::mfma(tk, wa[t], accB[mb]);  // W_a K
         accC[mb] = TT::mfma(tk, pp[t], accC[mb]);
         accX[mb] = TT::mfma(tuv, pp[t], accX[mb]);
         accX[mb] = TT::mfma(tv, pg[t], accX[mb]);
@@ -449,7 +448,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           if (!(key < N && (!CAUSAL || key <= qi))) sc[r] = -INFINITY;
         }
       }
-      V wa[NK], wb[NK], pd[NK], pp[NK], pg[NK];
+      V wa[NK], wb[NK], pp[NK], pg[NK];
       auto elementwise = [&](int r) {
         const float p = fast_exp2(sc[r]);
         const float gv = gc[r] * tau;
@@ -478,7 +477,6 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           e0_p += vwb;
           vset<TT>(wa[kk], ss, p * t1);
           vset<TT>(wb[kk], ss, vwb);
-          vset<TT>(pd[kk], ss, p * dpv);
           vset<TT>(pp[kk], ss, p);
           vset<TT>(pg[kk], ss, vpg);
         }
@@ -549,7 +547,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
           accX[mb] = TT::mfma(o[2], pg[t], accX[mb]);  // dPbar V
         } else {
           accA[mb] = TT::mfma(o[1], wa[t], accA[mb]);
-          accB[mb] = TT::mfma(o[0], pd[t], accB[mb]);
+          accB[mb] = TT::mfma(o[0], wa[t], accB[mb]);  // W_a K
           accX[mb] = TT::mfma(o[3], pp[t], accX[mb]);
           accA[mb] = TT::mfma(o[0], wb[t], accA[mb]);
           accC[mb] = TT::mfma(o[0], pp[t], accC[mb]);

@@ -3,10 +3,14 @@
 // FlashBoB review page (Summary; Strengths on Prop. 4.1): alpha and E enter
 // gQ and gdO affinely, so each query row keeps alpha-free sums over the keys
 // and applies the two scalars once at the end:
-//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i (P dP) K - E_i P K ],
-//   gdO_i = (P UV + (P G) V) - alpha_i O_i,   E_i = sum_j W_b - alpha_i D_i.
-// A = W_a UK + W_b K, B = (P dP) K, C = P K and X = P UV + (P G) V are the
-// four float32 register tiles (head dims x 32 queries per wave).
+//   gQ_i  = tau [ (W_a UK + W_b K) - alpha_i W_a K - e0_i P K ],
+//   gdO_i = (P UV + (P G) V) - alpha_i O_i,
+//   e0_i = sum_j W_b,   E_i = e0_i - alpha_i D_i.
+// A = W_a UK + W_b K, B = W_a K, C = P K and X = P UV + (P G) V are the four
+// float32 register tiles (head dims x 32 queries per wave). With E written out,
+// gQ = tau [A - alpha (P dP) K - E P K]; since W_a K = (P dP) K - D P K, taking
+// B = W_a K and the e0 coefficient is the same value and lets A and B share the
+// weight tile W_a (one weight tile fewer per step).
 #pragma once
 
 #include "common.hpp"
@@ -56,7 +60,7 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r4 * 4 + e;
-        q[e] = tau * (A[mbl][r] - alpha * B[mbl][r] - E * C[mbl][r]);
+        q[e] = tau * (A[mbl][r] - alpha * B[mbl][r] - e0 * C[mbl][r]);
         x[e] = X[mbl][r] - alpha * o[e];
       }
       store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
