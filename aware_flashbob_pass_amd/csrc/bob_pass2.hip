@@ -241,12 +241,18 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   auto scal = [&](int j) { return reinterpret_cast<float*>(lds + (j % NBUF) * STAGE_ELEMS + NT * G::ROW_ELEMS); };
   auto active = [&](int j) { return !CAUSAL || (it_begin + j) * kTile + kTile - 1 >= k0w; };
 
-  float sreg = 0.f;  // one of the 4 x 32 row scalars of a later stage (threads 0..127)
+  // Row scalars staged per query: L log2(e), D, alpha and c = alpha D + E, so that
+  // Sbar = P (Pbar - E) = dPbar (dP - D) + P (H - c) (Pbar = G (dP - D) - alpha dP + H).
+  float sreg = 0.f;  // one of the NSCAL x 32 row scalars of a later stage
   auto load_scal = [&](int i0) {
     sreg = 0.f;
     if (tid < NSCAL * kTile) {
       const int which = tid / kTile, row = i0 + tid % kTile;
-      if (row < N) sreg = vsrc[which][row] * (which == 0 ? kLog2e : 1.f);
+      if (row < N) {
+        if (which == 0) sreg = vsrc[0][row] * kLog2e;
+        else if (which == 3) sreg = fmaf(vsrc[2][row], vsrc[1][row], vsrc[3][row]);
+        else sreg = vsrc[which][row];
+      }
     }
   };
   auto put_scal = [&](int stg) {
@@ -314,13 +320,13 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
         }
       }
       V wds[NK], wsb[NK], wdp[NK];
-      f32x4 d4, a4, e4;  // D, alpha, E of the current group of 4 rows (loaded at its first row)
+      f32x4 d4, a4, c4;  // D, alpha, c of the current group of 4 rows (loaded at its first row)
       auto elementwise = [&](int r) {
         if ((r & 3) == 0) {
           d4 = row4(1, r >> 2);
           if constexpr (!FIRST) {
             a4 = row4(2, r >> 2);
-            e4 = row4(3, r >> 2);
+            c4 = row4(3, r >> 2);
           }
         }
         const float dq = d4[r & 3];
@@ -332,10 +338,9 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
         if constexpr (FIRST) {
           vset<TT>(wdp[kk], ss, p);  // P
         } else {
-          const float al = a4[r & 3], eq = e4[r & 3];
-          const float gv = gc[r] * tau;
-          vset<TT>(wsb[kk], ss, p * (fmaf(gv, t1, hc[r]) - fmaf(al, dpv, eq)));  // Sbar
-          vset<TT>(wdp[kk], ss, p * (gv - al));                                  // dPbar
+          const float dpb = p * (gc[r] * tau - a4[r & 3]);           // dPbar = P (G - alpha)
+          vset<TT>(wsb[kk], ss, fmaf(dpb, t1, p * (hc[r] - c4[r & 3])));  // Sbar
+          vset<TT>(wdp[kk], ss, dpb);
         }
       };
 #pragma unroll
