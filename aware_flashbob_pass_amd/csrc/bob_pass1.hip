@@ -309,7 +309,11 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   using T = typename TT::elem;
   using V = typename TT::vec;
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
-  constexpr int NT = 4, NBUF = 3;
+  // d = 64: four LDS stages, copies issued three steps ahead from inline assembly
+  // and awaited one step before use; d = 128 (no register room for the deeper
+  // unroll) keeps three stages, two steps ahead, compiler-visible copies.
+  constexpr bool DEEP = D == 64;
+  constexpr int NT = 4, NBUF = DEEP ? 4 : 3, AHEAD = NBUF - 1;
   // d = 64 keeps the next step's score tiles in registers (software pipelining);
   // d = 128 has no room for them next to 256 accumulator registers and forms
   // each step's score tiles at the start of the step instead.
@@ -318,6 +322,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
   constexpr bool NEED_G = MODE != kDqPass;      // the first backward needs S and dP only
   constexpr bool NEED_H = NEED_DP && NEED_G;
+  // direct copies one wave issues per step (K always, V for dP, UK for G, UV for H)
+  constexpr int COPIES = (1 + NEED_DP + NEED_G + NEED_H) * stage_copies<D, kBlock / 64>();
   constexpr int NH = TWO ? P1<TT, D>::NH : 1;
   constexpr int MBA = TWO ? P1<TT, D>::MBA : MB;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
@@ -372,10 +378,17 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       if (NEED_TILE[t])
-        stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS,
-                                          wave, lane);
+        stage_direct<TT, D, kBlock / 64, DEEP>(src[t], (kt_begin + j) * kTile, N,
+                                                lds + (stg * NT + t) * G::ROW_ELEMS, wave, lane);
   };
-  for (int j = 0; j < 2 && j < nsteps; ++j) issue(j, j);
+  // The stage copies are invisible to the compiler (inline assembly), so make it
+  // complete its own loads of the resident rows and row scalars here: otherwise it
+  // could wait for them inside the loop with a vmcnt(0) that also drains the copies.
+  if constexpr (DEEP) {
+    settle_regs(bq, bdo, lq, dq, al, er);
+    if constexpr (NEED_G) settle_regs(buq);
+  }
+  for (int j = 0; j < AHEAD && j < nsteps; ++j) issue(j, j);
   wait_vmem();
   __syncthreads();
 
@@ -399,10 +412,14 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   }
 
   // One pipeline step; S = j % NBUF is a compile-time constant so that every LDS
-  // address is a loop-invariant per-lane offset plus an immediate.
+  // address is a loop-invariant per-lane offset plus an immediate. Step j reads
+  // stage S (and S + 1 for the next step's scores) and copies step j + AHEAD into
+  // stage S + AHEAD (last read in step j - 1). With DEEP it then waits, before its
+  // barrier, only for the copies of step j - 1 (step j + 2, read from step j + 1
+  // on), so each copy has two steps to land; otherwise for all of them.
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
-    constexpr int SN = (S + 1) % NBUF, SC = (S + 2) % NBUF;
+    constexpr int SN = (S + 1) % NBUF, SC = (S + AHEAD) % NBUF;
     const T* ck = lds + (S * NT + 0) * G::ROW_ELEMS;
     const T* cv = lds + (S * NT + 1) * G::ROW_ELEMS;
     const T* cuk = lds + (S * NT + 2) * G::ROW_ELEMS;
@@ -411,7 +428,8 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     const T* nv = lds + (SN * NT + 1) * G::ROW_ELEMS;
     const T* nuk = lds + (SN * NT + 2) * G::ROW_ELEMS;
     const T* nuv = lds + (SN * NT + 3) * G::ROW_ELEMS;
-    if (j + 2 < nsteps) issue(SC, j + 2);  // buffer SC was last read in step j - 1
+    const bool copies = j + AHEAD < nsteps;
+    if (copies) issue(SC, j + AHEAD);
     const bool act = active(j);
     const bool act_next = (j + 1 < nsteps) && active(j + 1);
     const int k0 = (kt_begin + j) * kTile;
@@ -578,20 +596,13 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
       pc = px;
       hc = hx;
     }
-    wait_vmem();
+    if (DEEP && copies) wait_vmem_keep<COPIES>();  // this step's copies may stay in flight
+    else wait_vmem();
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   int j = 0;
-  for (; j + NBUF <= nsteps; j += NBUF) {
-    step(I0{}, j);
-    step(I1{}, j + 1);
-    step(I2{}, j + 2);
-  }
-  if (j < nsteps) step(I0{}, j);
-  if (j + 1 < nsteps) step(I1{}, j + 1);
+  for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
+  unroll_steps_until(step, j, nsteps, std::make_integer_sequence<int, NBUF - 1>{});
 
   if constexpr (TWO) {
     if (a.nsplit == 1) {
@@ -646,7 +657,7 @@ template <class TT, int D>
 static size_t pass1_lds_bytes() {
   using G = Geo<TT, D>;
   if constexpr (TT::KPL == 1) return (size_t)4 * (G::ROW_ELEMS + G::T_ELEMS) * sizeof(typename TT::elem);
-  return (size_t)3 * 4 * G::ROW_ELEMS * sizeof(typename TT::elem);
+  return (size_t)(D == 64 ? 4 : 3) * 4 * G::ROW_ELEMS * sizeof(typename TT::elem);  // stages of K, V, UK, UV
 }
 
 template <class TT, int D, bool CAUSAL>

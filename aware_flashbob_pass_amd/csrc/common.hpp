@@ -21,6 +21,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <stdint.h>
 
 namespace fb {
@@ -194,14 +196,37 @@ __device__ inline void load_resident(const typename TT::elem* __restrict__ src, 
   }
 }
 
+// One direct global -> LDS copy: global_load_lds_dwordx4, whose lane L writes
+// the 16 bytes at the wave-uniform LDS address `lds` + 16 L (the address goes in
+// M0). ASYNC = false uses the compiler builtin; the compiler cannot tell which
+// LDS bytes such a copy writes, so it waits for the copy to land before the
+// wave's next LDS read. ASYNC = true issues the same instruction from inline
+// assembly, invisible to the compiler, so copies stay in flight across LDS reads
+// and barriers; the kernel then orders them itself with s_waitcnt vmcnt before
+// the barrier that publishes a stage (the s_nop covers the M0 write -> LDS-DMA
+// hazard).
+template <bool ASYNC>
+__device__ inline void glds16(const void* gsrc, void* lds) {
+  if constexpr (ASYNC) {
+    const unsigned m0 =
+        __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) void*)lds);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+  } else {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  }
+}
+
 // Direct global -> LDS staging of one 32-row stage of a [N][D] tensor (16-bit
-// types): each wave issues global_load_lds_dwordx4, whose lane L writes the 16
-// bytes at (wave-uniform LDS base) + 16 L. LDS slot s of the tile is row
-// s / (D / 8), physical chunk s % (D / 8); its source is the logical chunk
-// (physical chunk ^ swz(row)) of that row, which realises the XOR swizzle of
-// roff(). Rows >= N fetch row N - 1 (finite values; every consumer masks them
-// out). Completion: s_waitcnt vmcnt(0) then a workgroup barrier.
-template <class TT, int D, int NWAVES>
+// types) with glds16. LDS slot s of the tile is row s / (D / 8), physical chunk
+// s % (D / 8); its source is the logical chunk (physical chunk ^ swz(row)) of
+// that row, which realises the XOR swizzle of roff(). Rows >= N fetch row
+// N - 1 (finite values; every consumer masks them out). Each wave issues
+// stage_copies<D, NWAVES>() copies. Completion: s_waitcnt vmcnt then a
+// workgroup barrier.
+template <int D, int NWAVES>
+__host__ __device__ constexpr int stage_copies() { return kTile * (D / 8) / (64 * NWAVES); }
+
+template <class TT, int D, int NWAVES, bool ASYNC = false>
 __device__ inline void stage_direct(const typename TT::elem* __restrict__ src, int r0, int N,
                                     typename TT::elem* tile, int wave, int lane) {
   static_assert(sizeof(typename TT::elem) == 2, "16-bit types only");
@@ -215,13 +240,51 @@ __device__ inline void stage_direct(const typename TT::elem* __restrict__ src, i
     const int row = slot / SPR, pc = slot % SPR;
     const int c = pc ^ swz<D>(row);
     const int grow = min(r0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (size_t)grow * D + c * 8),
-                                     (__attribute__((address_space(3))) void*)(tile + blk * 64 * 8),
-                                     16, 0, 0);
+    glds16<ASYNC>(src + (size_t)grow * D + c * 8, tile + blk * 64 * 8);
   }
 }
 
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Unrolled runs of pipeline steps with compile-time stage indices: unroll_steps
+// calls f(integral_constant<int, I>, j0 + I) for every I of the sequence;
+// unroll_steps_until does so only while j0 + I < end (a loop's tail).
+template <class F, int... I>
+__device__ inline void unroll_steps(F& f, int j0, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}, j0 + I), ...);
+}
+template <class F, int... I>
+__device__ inline void unroll_steps_until(F& f, int j0, int end, std::integer_sequence<int, I...>) {
+  ((j0 + I < end ? f(std::integral_constant<int, I>{}, j0 + I) : void()), ...);
+}
+
+// Make the compiler complete the loads that produced these registers here (an
+// empty asm that reads them), before a loop that keeps inline-assembly copies in
+// flight across its own s_waitcnt vmcnt(N).
+template <class R>
+__device__ inline void settle_one(const R& r) {
+  asm volatile("" ::"v"(r));
+}
+template <class... R>
+__device__ inline void settle_regs(const R&... r) {
+  (settle_one(r), ...);
+}
+template <class V, int K>
+__device__ inline void settle_regs(const V (&r)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) settle_one(r[k]);
+}
+template <class V, int K, class... R>
+__device__ inline void settle_regs(const V (&r)[K], const R&... rest) {
+  settle_regs(r);
+  settle_regs(rest...);
+}
+
+// All but the newest N vector-memory operations of the wave have completed.
+template <int N>
+__device__ inline void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
