@@ -178,7 +178,9 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
 }
 
 // Staged variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
-// tiles plus their four row scalars, loaded two steps ahead; transposed
+// tiles plus their four row scalars, copied two steps ahead from inline
+// assembly so that the end of a step waits only for the copies of the next one
+// (the compiler does not see them and inserts no wait of its own); transposed
 // operands come from the transposing LDS load. Each step forms its score tiles,
 // its weights and its accumulating products in turn. At d = 64 the kernel fits
 // 256 registers, so two waves share each SIMD (two workgroups per CU) and each
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   using T = typename TT::elem;
   using V = typename TT::vec;
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
-  constexpr int NT = 3, NBUF = 3;
+  constexpr int NT = 3, NBUF = 3, AHEAD = NBUF - 1;
   constexpr int STAGE_ELEMS = NT * G::ROW_ELEMS + 4 * kTile * 4 / (int)sizeof(T);  // tiles + 4 x 32 floats
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -208,6 +210,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   // FIRST (the first backward g: dK = tau dS^T Q, dV = P^T dO) needs S and dP only:
   // no UQ tile, no UK / UV rows, and only the L and D row scalars.
   constexpr int NSCAL = FIRST ? 2 : 4;
+  constexpr int COPIES = (FIRST ? 2 : 3) * stage_copies<D, kBlock / 64>() + 1;  // per wave and stage
   const float* vsrc[4] = {a.L + vbase, a.D + vbase, FIRST ? nullptr : a.alpha + vbase,
                           FIRST ? nullptr : a.E + vbase};
   const int k0w = kt * kBlockRows + wave * kTile;
@@ -241,34 +244,23 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   auto scal = [&](int j) { return reinterpret_cast<float*>(lds + (j % NBUF) * STAGE_ELEMS + NT * G::ROW_ELEMS); };
   auto active = [&](int j) { return !CAUSAL || (it_begin + j) * kTile + kTile - 1 >= k0w; };
 
-  // Row scalars staged per query: L log2(e), D, alpha and c = alpha D + E, so that
-  // Sbar = P (Pbar - E) = dPbar (dP - D) + P (H - c) (Pbar = G (dP - D) - alpha dP + H).
-  float sreg = 0.f;  // one of the NSCAL x 32 row scalars of a later stage
-  auto load_scal = [&](int i0) {
-    sreg = 0.f;
-    if (tid < NSCAL * kTile) {
-      const int which = tid / kTile, row = i0 + tid % kTile;
-      if (row < N) {
-        if (which == 0) sreg = vsrc[0][row] * kLog2e;
-        else if (which == 3) sreg = fmaf(vsrc[2][row], vsrc[1][row], vsrc[3][row]);
-        else sreg = vsrc[which][row];
-      }
-    }
-  };
-  auto put_scal = [&](int stg) {
-    if (tid < NSCAL * kTile) scal(stg)[tid] = sreg;
-  };
+  // Each stage also holds the row scalars L, D, alpha, E of its 32 queries (rows
+  // >= N repeat row N - 1); wave w copies scalar w % NSCAL with its lanes 0..31,
+  // so every wave issues the same number of copies per stage (with NSCAL = 2 two
+  // waves write the same values). The step forms L log2(e) and c = alpha D + E, so
+  // that Sbar = P (Pbar - E) = dPbar (dP - D) + P (H - c) (Pbar = G (dP - D) -
+  // alpha dP + H).
   auto issue = [&](int stg, int j) {
+    const int i0 = (it_begin + j) * kTile;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      if (!FIRST || t < 2) stage_direct<TT, D, kBlock / 64>(src[t], (it_begin + j) * kTile, N, tile(stg, t), wave, lane);
+      if (!FIRST || t < 2) stage_direct<TT, D, kBlock / 64, true>(src[t], i0, N, tile(stg, t), wave, lane);
+    const int which = wave % NSCAL;
+    if (lane < kTile) glds4<true>(vsrc[which] + min(i0 + lane, N - 1), scal(stg) + which * kTile);
   };
-  for (int j = 0; j < 2 && j < nsteps; ++j) {
-    issue(j, j);
-    load_scal((it_begin + j) * kTile);
-    put_scal(j);
-  }
-  if (nsteps > 2) load_scal((it_begin + 2) * kTile);
+  settle_regs(bk, bv);
+  if constexpr (!FIRST) settle_regs(buk, buv);
+  for (int j = 0; j < AHEAD && j < nsteps; ++j) issue(j, j);
   wait_vmem();
   __syncthreads();
 
@@ -287,11 +279,9 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   };
   auto step = [&](auto S_c, int j) {
     constexpr int S = decltype(S_c)::value;
-    if (j + 2 < nsteps) {  // buffer (S + 2) % NBUF was last read in step j - 1
-      issue((S + 2) % NBUF, j + 2);
-      put_scal((S + 2) % NBUF);
-    }
-    if (j + 3 < nsteps) load_scal((it_begin + j + 3) * kTile);
+    constexpr int SC = (S + AHEAD) % NBUF;
+    const bool copies = j + AHEAD < nsteps;
+    if (copies) issue(SC, j + AHEAD);  // buffer SC was last read in step j - 1
     const int i0 = (it_begin + j) * kTile;
     if (active(j)) {
       sc = zero16();
@@ -308,7 +298,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
       };
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = row4(0, r4);
+        const f32x4 l4 = row4(0, r4) * kLog2e;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[r4 * 4 + e] = sc[r4 * 4 + e] * cs - l4[e];
       }
@@ -326,7 +316,9 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
           d4 = row4(1, r >> 2);
           if constexpr (!FIRST) {
             a4 = row4(2, r >> 2);
-            c4 = row4(3, r >> 2);
+            const f32x4 e4 = row4(3, r >> 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c4[e] = fmaf(a4[e], d4[e], e4[e]);
           }
         }
         const float dq = d4[r & 3];
@@ -367,20 +359,13 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
           accV[mb] = TT::mfma(tdo, wdp[t], accV[mb]);    // P^T dO or dPbar^T dO
         }
     }
-    wait_vmem();
+    if (copies) wait_vmem_keep<COPIES>();  // this step's copies may stay in flight
+    else wait_vmem();
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   int j = 0;
-  for (; j + NBUF <= nsteps; j += NBUF) {
-    step(I0{}, j);
-    step(I1{}, j + 1);
-    step(I2{}, j + 2);
-  }
-  if (j < nsteps) step(I0{}, j);
-  if (j + 1 < nsteps) step(I1{}, j + 1);
+  for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
+  unroll_steps_until(step, j, nsteps, std::make_integer_sequence<int, NBUF - 1>{});
 
   if (a.nsplit == 1) {
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);

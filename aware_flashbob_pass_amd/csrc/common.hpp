@@ -216,6 +216,18 @@ __device__ inline void glds16(const void* gsrc, void* lds) {
   }
 }
 
+// The same for 4 bytes per lane: lane l's value lands at lds + 4 l.
+template <bool ASYNC>
+__device__ inline void glds4(const void* gsrc, void* lds) {
+  if constexpr (ASYNC) {
+    const unsigned m0 =
+        __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) void*)lds);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+  } else {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+  }
+}
+
 // Direct global -> LDS staging of one 32-row stage of a [N][D] tensor (16-bit
 // types) with glds16. LDS slot s of the tile is row s / (D / 8), physical chunk
 // s % (D / 8); its source is the logical chunk (physical chunk ^ swz(row)) of
