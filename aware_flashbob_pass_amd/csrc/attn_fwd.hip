@@ -57,11 +57,17 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // tiles in three row-major LDS stages loaded two steps ahead; each step forms
 // its score tile, runs the online softmax and accumulates P V, reading V^T
 // operands with the transposing LDS load. At d = 64 three to four waves share
-// each SIMD, which hides more than forming the next step's tile early did. The
-// running rescale of the accumulators is skipped when no row maximum of the wave
-// grew.
+// each SIMD, which hides more than forming the next step's tile early did.
+// The reference maximum m of a row moves only when some row of the wave sees a
+// score more than 2^kRescaleLog2 above its own m (log2 domain): until then the
+// weights 2^(s - m) may exceed 1 by up to that factor, which float32 sums and the
+// 16-bit weight operands hold with unchanged relative precision, and the result
+// is the same because the denominator l and the accumulators share m. This skips
+// most accumulator rescales after the first steps.
 // With `nsplit` > 1 each split covers a key range and writes a record
 // (accumulators, max, partial denominators) that fwd_combine merges.
+constexpr float kRescaleLog2 = 8.f;
+
 template <class TT, int D, bool CAUSAL, bool WITH_D>
 __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(Fwd
       if (fold) mx *= cs;
       mx = pair_max32(mx);
       const float mnew = fmaxf(m, mx);
-      if (__ballot(mnew > m)) {
+      if (__ballot(mnew > m + kRescaleLog2)) {
         const float f = fast_exp2(m - mnew);
         l *= f;
 #pragma unroll

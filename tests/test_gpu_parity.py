@@ -187,6 +187,36 @@ def test_attn_fwd_stats(dtype, d, causal):
     assert rel(dvec.cpu().double().numpy(), d_ref) <= tol
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stats_growing_row_maxima(causal, d):
+    """Key rows scaled by a ramp make every row maximum creep up over the keys (most
+    steps below the online softmax's rescale threshold), and a block of ten late keys
+    scaled by 4 makes it jump far above it; L, D, O and the BoB outputs must still
+    match the oracle."""
+    fb = _fb()
+    w = workload.custom(1, 2, 1000, d, "bf16", causal)
+    cpu = workload.make_inputs(w, 11)
+    N = w.N
+    k = cpu["K"].float() * torch.linspace(0.5, 3.0, N).view(1, 1, N, 1)
+    k[:, :, N - 40:N - 30, :] *= 4.0
+    cpu["K"] = k.to(cpu["K"].dtype)
+    g = {n: v.cuda() for n, v in cpu.items()}
+    _note(f"case growing maxima d={d} causal={causal}")
+    o, lse, dvec = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=causal, do=g["dO"])
+    out = _run_bob(fb, g, w)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), w.scale, causal)
+    _, _, _, d_ref = oracle.first_backward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), to_f64(cpu["dO"]),
+                                           w.scale, causal)
+    assert float(np.max(np.abs(l_ref))) > 10.0  # scores span far more than 2^8 in the exponent
+    assert rel(to_f64(o.cpu()), o_ref) <= TOL["bf16"]
+    assert rel(lse.cpu().double().numpy(), l_ref) <= 1e-3
+    assert rel(dvec.cpu().double().numpy(), d_ref) <= TOL["bf16"]
+    errs = call_errors({k_: to_f64(x.cpu()) for k_, x in zip(OUTS, out)}, _oracle_full(cpu, w))
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
 @pytest.mark.parametrize("dtype,d,causal", [("fp32", 64, False), ("fp32", 128, True), ("bf16", 64, True),
                                             ("bf16", 128, False), ("fp16", 64, False)])
 def test_attn_bwd(dtype, d, causal):
