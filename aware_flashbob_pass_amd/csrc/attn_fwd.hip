@@ -56,8 +56,9 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // Staged variant for 16-bit inputs (same staging scheme as pass 1): K and V
 // tiles in three row-major LDS stages loaded two steps ahead; each step forms
 // its score tile, runs the online softmax and accumulates P V, reading V^T
-// operands with the transposing LDS load. At d = 64 three to four waves share
-// each SIMD, which hides more than forming the next step's tile early did.
+// operands with the transposing LDS load. Declared for two waves per SIMD (the
+// register form; d = 128 then needs 188 VGPRs and no AGPRs), which hides more
+// than forming the next step's tile early did.
 // The reference maximum m of a row moves only when some row of the wave sees a
 // score more than 2^kRescaleLog2 above its own m (log2 domain): until then the
 // weights 2^(s - m) may exceed 1 by up to that factor, which float32 sums and the
@@ -69,7 +70,7 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 constexpr float kRescaleLog2 = 8.f;
 
 template <class TT, int D, bool CAUSAL, bool WITH_D>
-__global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
