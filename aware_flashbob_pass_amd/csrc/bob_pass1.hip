@@ -621,36 +621,53 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
 }
 
 // Sum the split records of each wave in split order, then apply the epilogue.
+// Sum the split records of one 32-wide head-dim block per workgroup (grid z =
+// half x block) in split order, two splits' loads in flight at a time, and apply
+// the epilogue to that block; every block forms the same alpha_i and e0_i, and
+// block 0 writes them.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) {
   constexpr int MB = P1<TT, D>::MBA;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
-  const int N = a.N, bh = blockIdx.y, half = blockIdx.z;
+  const int bh = blockIdx.y, half = blockIdx.z / MB, mbl = blockIdx.z % MB;
   const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
-  f32x16 A[MB], B[MB], C[MB], X[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    A[mb] = zero16();
-    B[mb] = zero16();
-    C[mb] = zero16();
-    X[mb] = zero16();
-  }
+  f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};  // A, B, C, X of block mbl
   float alpha_p = 0.f, e0_p = 0.f;
-  for (int sp = 0; sp < a.nsplit; ++sp) {
-    const float* R = pass1_record<TT, D>(a, sp, bh, blockIdx.x, wave, half);
+  auto rec = [&](int sp) { return pass1_record<TT, D>(a, sp, bh, blockIdx.x, wave, half); };
+  int sp = 0;
+  for (; sp + 2 <= a.nsplit; sp += 2) {
+    const float* R0 = rec(sp);
+    const float* R1 = rec(sp + 1);
+    f32x16 v0[4], v1[4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      A[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-      B[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
-      C[mb] += load_acc16(R + ((2 * MB + mb) * 64 + lane) * 16);
-      X[mb] += load_acc16(R + ((3 * MB + mb) * 64 + lane) * 16);
+    for (int k = 0; k < 4; ++k) {
+      v0[k] = load_acc16(R0 + ((k * MB + mbl) * 64 + lane) * 16);
+      v1[k] = load_acc16(R1 + ((k * MB + mbl) * 64 + lane) * 16);
     }
+    const float a0 = R0[P1<TT, D>::ACC_FLOATS + lane], e0 = R0[P1<TT, D>::ACC_FLOATS + 64 + lane];
+    const float a1 = R1[P1<TT, D>::ACC_FLOATS + lane], e1 = R1[P1<TT, D>::ACC_FLOATS + 64 + lane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += v0[k];
+      acc[k] += v1[k];
+    }
+    alpha_p += a0;
+    alpha_p += a1;
+    e0_p += e0;
+    e0_p += e1;
+  }
+  if (sp < a.nsplit) {
+    const float* R = rec(sp);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += load_acc16(R + ((k * MB + mbl) * 64 + lane) * 16);
     alpha_p += R[P1<TT, D>::ACC_FLOATS + lane];
     e0_p += R[P1<TT, D>::ACC_FLOATS + 64 + lane];
   }
-  (void)N;
-  pass1_epilogue<TT, D>(A, B, C, X, alpha_p, e0_p, qi, g, bh, half, a);
+  const float alpha = pair_sum32(alpha_p);
+  const float e0 = pair_sum32(e0_p);
+  pass1_epilogue_block<TT, D>(acc[0], acc[1], acc[2], acc[3], alpha, e0, qi, g, bh, half * MB + mbl, a);
+  if (blockIdx.z == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
 }
 
 template <class TT, int D>
@@ -692,7 +709,7 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_c1_t(const Pass1Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH, P1<TT, D>::NH);
+  dim3 grid(row_tiles(a.N), a.BH, P1<TT, D>::NH * P1<TT, D>::MBA);
   hipLaunchKernelGGL((bob_pass1_combine_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

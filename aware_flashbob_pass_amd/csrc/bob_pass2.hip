@@ -22,9 +22,8 @@
 namespace fb {
 
 template <class TT, int D>
-__device__ inline void pass2_epilogue(const f32x16 (&dK)[Geo<TT, D>::MB], const f32x16 (&dV)[Geo<TT, D>::MB],
-                                      int kj, int g, int bh, const Pass2Args& a) {
-  using G = Geo<TT, D>;
+__device__ inline void pass2_epilogue_block(const f32x16& dK, const f32x16& dV, int kj, int g, int bh, int mb,
+                                            const Pass2Args& a) {
   using T = typename TT::elem;
   if (kj >= a.N) return;
   const size_t row = (size_t)bh * a.N + kj;
@@ -32,14 +31,19 @@ __device__ inline void pass2_epilogue(const f32x16 (&dK)[Geo<TT, D>::MB], const 
   T* gV = reinterpret_cast<T*>(a.gV) + row * D;
   const float tau = a.tau;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int dim = mb * 32 + kappa(r4 * 4, g);
+    const int r = r4 * 4;
+    store4<TT>(gK + dim, tau * dK[r], tau * dK[r + 1], tau * dK[r + 2], tau * dK[r + 3]);
+    store4<TT>(gV + dim, dV[r], dV[r + 1], dV[r + 2], dV[r + 3]);
+  }
+}
+
+template <class TT, int D>
+__device__ inline void pass2_epilogue(const f32x16 (&dK)[Geo<TT, D>::MB], const f32x16 (&dV)[Geo<TT, D>::MB],
+                                      int kj, int g, int bh, const Pass2Args& a) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dim = mb * 32 + kappa(r4 * 4, g);
-      const int r = r4 * 4;
-      store4<TT>(gK + dim, tau * dK[mb][r], tau * dK[mb][r + 1], tau * dK[mb][r + 2], tau * dK[mb][r + 3]);
-      store4<TT>(gV + dim, dV[mb][r], dV[mb][r + 1], dV[mb][r + 2], dV[mb][r + 3]);
-    }
+  for (int mb = 0; mb < Geo<TT, D>::MB; ++mb) pass2_epilogue_block<TT, D>(dK[mb], dV[mb], kj, g, bh, mb, a);
 }
 
 template <class TT, int D>
@@ -374,31 +378,42 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   pass2_write_record<TT, D>(accK, accV, split, bh, kt, wave, lane, a);
 }
 
+// Sum the split records of one 32-wide head-dim block per workgroup (grid z) in
+// split order, four splits' loads in flight at a time, and write that block.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
-  using G = Geo<TT, D>;
-  constexpr int MB = G::MB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  constexpr int MB = Geo<TT, D>::MB;
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.y, mb = blockIdx.z;
   const int kj = blockIdx.x * kBlockRows + wave * kTile + n;
   const int kt_count = row_tiles(a.N);
-  f32x16 dK[MB], dV[MB];
+  auto rec = [&](int sp) {
+    return a.part + ((((size_t)sp * a.BH + bh) * kt_count + blockIdx.x) * 4 + wave) * pass2_record_floats(D);
+  };
+  f32x16 dK = zero16(), dV = zero16();
+  int sp = 0;
+  for (; sp + U <= a.nsplit; sp += U) {
+    f32x16 k[U], v[U];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    dK[mb] = zero16();
-    dV[mb] = zero16();
-  }
-  for (int sp = 0; sp < a.nsplit; ++sp) {
-    const size_t rec = (((size_t)sp * a.BH + bh) * kt_count + blockIdx.x) * 4 + wave;
-    const float* R = a.part + rec * pass2_record_floats(D);
+    for (int u = 0; u < U; ++u) {
+      const float* R = rec(sp + u);
+      k[u] = load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+      v[u] = load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+    }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      dK[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-      dV[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+    for (int u = 0; u < U; ++u) {
+      dK += k[u];
+      dV += v[u];
     }
   }
-  pass2_epilogue<TT, D>(dK, dV, kj, g, bh, a);
+  for (; sp < a.nsplit; ++sp) {
+    const float* R = rec(sp);
+    dK += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+    dV += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+  }
+  pass2_epilogue_block<TT, D>(dK, dV, kj, g, bh, mb, a);
 }
 
 template <class TT, int D>
@@ -465,7 +480,7 @@ hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_r2_t(const Pass2Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH);
+  dim3 grid(row_tiles(a.N), a.BH, Geo<TT, D>::MB);
   hipLaunchKernelGGL((bob_pass2_reduce_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

@@ -30,6 +30,44 @@ struct P1 {
   static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
 };
 
+// gQ_i and gdO_i over the 32-wide head-dim block `mbg` from its alpha-free sums,
+// with alpha_i and e0_i already summed over the lane pair of the row.
+template <class TT, int D>
+__device__ inline void pass1_epilogue_block(const f32x16& A, const f32x16& B, const f32x16& C, const f32x16& X,
+                                            float alpha, float e0, int qi, int g, int bh, int mbg,
+                                            const Pass1Args& a) {
+  using T = typename TT::elem;
+  const int N = a.N;
+  if (qi >= N) return;
+  const size_t row = (size_t)bh * N + qi;
+  const T* O = reinterpret_cast<const T*>(a.O) + row * D;
+  T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
+  T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
+  const float tau = a.tau;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int dim = mbg * 32 + kappa(r4 * 4, g);
+    float o[4], q[4], x[4];
+    load4<TT>(O + dim, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r4 * 4 + e;
+      q[e] = tau * (A[r] - alpha * B[r] - e0 * C[r]);
+      x[e] = X[r] - alpha * o[e];
+    }
+    store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
+    store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
+  }
+}
+
+// alpha_i and E_i = e0_i - alpha_i D_i of the row (lane group 0 writes).
+__device__ inline void pass1_write_scalars(float alpha, float e0, int qi, int g, int bh, const Pass1Args& a) {
+  if (qi >= a.N || g != 0) return;
+  const size_t row = (size_t)bh * a.N + qi;
+  a.alpha[row] = alpha;
+  a.E[row] = e0 - alpha * a.D[row];
+}
+
 // gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave (head-dim
 // blocks half * MBA .. half * MBA + MBA - 1).
 template <class TT, int D>
@@ -37,39 +75,13 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f
                                       const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
                                       float alpha_p, float e0_p, int qi, int g, int bh, int half,
                                       const Pass1Args& a) {
-  using T = typename TT::elem;
   constexpr int MBA = P1<TT, D>::MBA;
-  const int N = a.N;
   const float alpha = pair_sum32(alpha_p);
   const float e0 = pair_sum32(e0_p);
-  if (qi >= N) return;
-  const size_t row = (size_t)bh * N + qi;
-  const float dq = a.D[row];
-  const float E = e0 - alpha * dq;
-  const T* O = reinterpret_cast<const T*>(a.O) + row * D;
-  T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
-  T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
-  const float tau = a.tau;
 #pragma unroll
   for (int mbl = 0; mbl < MBA; ++mbl)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dim = (half * MBA + mbl) * 32 + kappa(r4 * 4, g);
-      float o[4], q[4], x[4];
-      load4<TT>(O + dim, o);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r4 * 4 + e;
-        q[e] = tau * (A[mbl][r] - alpha * B[mbl][r] - e0 * C[mbl][r]);
-        x[e] = X[mbl][r] - alpha * o[e];
-      }
-      store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
-      store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
-    }
-  if (g == 0 && half == 0) {
-    a.alpha[row] = alpha;
-    a.E[row] = E;
-  }
+    pass1_epilogue_block<TT, D>(A[mbl], B[mbl], C[mbl], X[mbl], alpha, e0, qi, g, bh, half * MBA + mbl, a);
+  if (half == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
 }
 
 // Raw accumulators and row partials of one wave for split `split`, half `half`.
