@@ -230,6 +230,13 @@ fb_status_t four_pass(const void* Q, const void* K, const void* V, const void* d
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
   static const char* names[3] = {"fourpass_alpha", "fourpass_energy", "fourpass_rows"};
   for (int sweep = 0; sweep < 3; ++sweep) {
+    // The scalar sweeps (and the rows sweep at d = 64) run two workgroups per CU,
+    // like the statistics kernel, so they take its split count. Record space: the
+    // scalar records (64 floats per wave) fit in the statistics records; the rows
+    // records (2 d / 32 tiles per wave) fit in the pass-1 records at up to twice
+    // the pass-1 split count.
+    if (sweep < 2) p1.nsplit = w.s0;
+    else p1.nsplit = (d == 64 && w.s1 > 1) ? std::min(w.s0, 2 * w.s1) : w.s1;
     fb_status_t st = run(names[sweep], s, [&] { return fb::launch_fourpass_sweep(p1, sweep, dt, d, causal, s); });
     if (st) return st;
   }

@@ -303,8 +303,16 @@ __device__ inline void pass1_schedule() {
 // the collapse saves: kAlphaPass sweeps the keys for alpha only (S and G),
 // kEnergyPass sweeps again for E with alpha known, and kRowsPass forms
 // gQ = tau (dS UK + Sbar K) and gdO = P UV + dPbar V with alpha and E known.
+// Waves per SIMD each pass-1 kernel is built for: the two-pass kernel keeps four
+// float32 accumulator tiles plus the next step's score tiles (one wave, AGPR
+// accumulators); the other modes hold at most two accumulator tiles, or at
+// d = 128 at most the alpha sweep's score tiles, and take the register form at two.
+__host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
+  return (mode == kTwoPass || (d == 128 && mode != kAlphaPass)) ? 1 : 2;
+}
+
 template <class TT, int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
+__global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   using V = typename TT::vec;
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
   // d = 64 keeps the next step's score tiles in registers (software pipelining);
   // d = 128 has no room for them next to 256 accumulator registers and forms
   // each step's score tiles at the start of the step instead.
-  constexpr bool PIPE = D == 64;
+  constexpr bool PIPE = D == 64 && MODE == kTwoPass;
   constexpr bool TWO = MODE == kTwoPass;
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
   constexpr bool NEED_G = MODE != kDqPass;      // the first backward needs S and dP only
@@ -599,6 +607,11 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_kernel(Pass1Args a) {
     if (DEEP && copies) wait_vmem_keep<COPIES>();  // this step's copies may stay in flight
     else wait_vmem();
     __syncthreads();
+    // The scalar sweeps' element-wise work has no memory effects; pin its sum to the
+    // step so the compiler cannot sink several steps' work (and keep their score
+    // tiles live) past the barriers.
+    if constexpr (MODE == kAlphaPass) asm volatile("" : "+v"(alpha_p)::"memory");
+    if constexpr (MODE == kEnergyPass) asm volatile("" : "+v"(e0_p)::"memory");
   };
   int j = 0;
   for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
