@@ -137,7 +137,7 @@ DT to_dt(fb_dtype_t t) { return t == FB_BF16 ? DT::BF16 : (t == FB_F16 ? DT::F16
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t o, l, dd, alpha, e, part, total;
+  size_t o, l, dd, alpha, e, l2, cc, part, total;
   int s0, s1, s2;  // splits of the statistics kernel, pass 1, pass 2
 };
 
@@ -157,6 +157,10 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   w.alpha = off;
   off += vec;
   w.e = off;
+  off += vec;
+  w.l2 = off;  // L log2(e) and c = alpha D + E, written by pass 1 for pass 2
+  off += vec;
+  w.cc = off;
   off += vec;
   const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
   const int nh = fb::pass1_halves(to_dt(dtype), d);
@@ -184,6 +188,8 @@ fb_status_t column_pass(const void* Q, const void* K, const void* V, const void*
   fb::Pass2Args p2{};
   p2.Q = Q; p2.K = K; p2.V = V; p2.dO = dO; p2.UQ = UQ; p2.UK = UK; p2.UV = UV;
   p2.L = L; p2.D = D; p2.alpha = alpha; p2.E = E; p2.gK = gK; p2.gV = gV;
+  p2.l2 = reinterpret_cast<const float*>(ws + w.l2);
+  p2.c = reinterpret_cast<const float*>(ws + w.cc);
   p2.part = reinterpret_cast<float*>(ws + w.part);
   p2.tau = tau; p2.N = N; p2.BH = BH; p2.nsplit = w.s2;
   fb_status_t st = run("bob_pass2", s, [&] { return fb::launch_pass2(p2, dt, d, causal, s); });
@@ -205,6 +211,8 @@ fb_status_t two_pass(const void* Q, const void* K, const void* V, const void* dO
   fb::Pass1Args p1{};
   p1.Q = Q; p1.K = K; p1.V = V; p1.dO = dO; p1.UQ = UQ; p1.UK = UK; p1.UV = UV; p1.O = O;
   p1.L = L; p1.D = D; p1.gQ = gQ; p1.gdO = gdO; p1.alpha = alpha; p1.E = E;
+  p1.l2 = reinterpret_cast<float*>(ws + w.l2);
+  p1.c = reinterpret_cast<float*>(ws + w.cc);
   p1.part = reinterpret_cast<float*>(ws + w.part);
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
   fb_status_t st = run("bob_pass1", s, [&] { return fb::launch_pass1(p1, dt, d, causal, s); });
@@ -226,6 +234,8 @@ fb_status_t four_pass(const void* Q, const void* K, const void* V, const void* d
   fb::Pass1Args p1{};
   p1.Q = Q; p1.K = K; p1.V = V; p1.dO = dO; p1.UQ = UQ; p1.UK = UK; p1.UV = UV; p1.O = O;
   p1.L = L; p1.D = D; p1.gQ = gQ; p1.gdO = gdO; p1.alpha = alpha; p1.E = E;
+  p1.l2 = reinterpret_cast<float*>(ws + w.l2);
+  p1.c = reinterpret_cast<float*>(ws + w.cc);
   p1.part = reinterpret_cast<float*>(ws + w.part);
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
   static const char* names[3] = {"fourpass_alpha", "fourpass_energy", "fourpass_rows"};

@@ -183,7 +183,11 @@ __device__ inline void fourpass_epilogue(const f32x16 (&Q)[D / 32], const f32x16
   if constexpr (MODE == kAlphaPass) {
     if (g == 0) a.alpha[row] = total;
   } else if constexpr (MODE == kEnergyPass) {
-    if (g == 0) a.E[row] = total;
+    if (g == 0) {  // alpha is known from the alpha sweep
+      a.E[row] = total;
+      a.l2[row] = a.L[row] * kLog2e;
+      a.c[row] = fmaf(a.alpha[row], a.D[row], total);
+    }
   } else if constexpr (MODE == kDqPass) {
     T* dQ = reinterpret_cast<T*>(a.gQ) + row * D;
     const float tau = a.tau;

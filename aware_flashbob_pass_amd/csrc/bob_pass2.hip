@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   // no UQ tile, no UK / UV rows, and only the L and D row scalars.
   constexpr int NSCAL = FIRST ? 2 : 4;
   constexpr int COPIES = (FIRST ? 2 : 3) * stage_copies<D, kBlock / 64>() + 1;  // per wave and stage
-  const float* vsrc[4] = {a.L + vbase, a.D + vbase, FIRST ? nullptr : a.alpha + vbase,
-                          FIRST ? nullptr : a.E + vbase};
+  const float* vsrc[4] = {(FIRST ? a.L : a.l2) + vbase, a.D + vbase, FIRST ? nullptr : a.alpha + vbase,
+                          FIRST ? nullptr : a.c + vbase};
   const int k0w = kt * kBlockRows + wave * kTile;
   const int kj = k0w + n;
 
@@ -248,12 +248,12 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   auto scal = [&](int j) { return reinterpret_cast<float*>(lds + (j % NBUF) * STAGE_ELEMS + NT * G::ROW_ELEMS); };
   auto active = [&](int j) { return !CAUSAL || (it_begin + j) * kTile + kTile - 1 >= k0w; };
 
-  // Each stage also holds the row scalars L, D, alpha, E of its 32 queries (rows
-  // >= N repeat row N - 1); wave w copies scalar w % NSCAL with its lanes 0..31,
-  // so every wave issues the same number of copies per stage (with NSCAL = 2 two
-  // waves write the same values). The step forms L log2(e) and c = alpha D + E, so
-  // that Sbar = P (Pbar - E) = dPbar (dP - D) + P (H - c) (Pbar = G (dP - D) -
-  // alpha dP + H).
+  // Each stage also holds the row scalars of its 32 queries (rows >= N repeat row
+  // N - 1): L log2(e), D, alpha and c = alpha D + E as pass 1 wrote them, so that
+  // Sbar = P (Pbar - E) = dPbar (dP - D) + P (H - c) (Pbar = G (dP - D) - alpha dP
+  // + H); the first backward stages L and D and scales L here. Wave w copies
+  // scalar w % NSCAL with its lanes 0..31, so every wave issues the same number of
+  // copies per stage (with NSCAL = 2 two waves write the same values).
   auto issue = [&](int stg, int j) {
     const int i0 = (it_begin + j) * kTile;
 #pragma unroll
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
       };
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = row4(0, r4) * kLog2e;
+        const f32x4 l4 = FIRST ? row4(0, r4) * kLog2e : row4(0, r4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[r4 * 4 + e] = sc[r4 * 4 + e] * cs - l4[e];
       }
@@ -320,9 +320,7 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
           d4 = row4(1, r >> 2);
           if constexpr (!FIRST) {
             a4 = row4(2, r >> 2);
-            const f32x4 e4 = row4(3, r >> 2);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) c4[e] = fmaf(a4[e], d4[e], e4[e]);
+            c4 = row4(3, r >> 2);
           }
         }
         const float dq = d4[r & 3];

@@ -30,7 +30,8 @@ struct Pass1Args {
   const float *L, *D;
   void *gQ, *gdO;
   float *alpha, *E;
-  float* part;  // split records (nsplit > 1)
+  float *l2, *c;  // per query for pass 2: L log2(e) and c = alpha D + E
+  float* part;    // split records (nsplit > 1)
   float tau;
   int N, BH, nsplit;
 };
@@ -39,6 +40,7 @@ struct Pass1Args {
 struct Pass2Args {
   const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
   const float *L, *D, *alpha, *E;
+  const float *l2, *c;  // L log2(e), c = alpha D + E (written by pass 1; staged 16-bit kernel)
   void *gK, *gV;
   float* part;
   float tau;

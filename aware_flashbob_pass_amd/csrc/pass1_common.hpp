@@ -60,12 +60,17 @@ __device__ inline void pass1_epilogue_block(const f32x16& A, const f32x16& B, co
   }
 }
 
-// alpha_i and E_i = e0_i - alpha_i D_i of the row (lane group 0 writes).
+// alpha_i and E_i = e0_i - alpha_i D_i of the row, and for pass 2 L_i log2(e) and
+// c_i = alpha_i D_i + E_i (lane group 0 writes).
 __device__ inline void pass1_write_scalars(float alpha, float e0, int qi, int g, int bh, const Pass1Args& a) {
   if (qi >= a.N || g != 0) return;
   const size_t row = (size_t)bh * a.N + qi;
+  const float dq = a.D[row];
+  const float E = e0 - alpha * dq;
   a.alpha[row] = alpha;
-  a.E[row] = e0 - alpha * a.D[row];
+  a.E[row] = E;
+  a.l2[row] = a.L[row] * kLog2e;
+  a.c[row] = fmaf(alpha, dq, E);
 }
 
 // gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave (head-dim
