@@ -241,6 +241,73 @@ def hutchinson_bench(args, name):
                    "probe": "rademacher"}}), flush=True)
 
 
+def max_n_probe(fb, workload, dev, args):
+    """Largest N (a power of two from 262144 up) whose call runs within the budget.
+
+    Each size runs once (the library is warmed by a small call first); the
+    next size is tried only if four times this call's time (the N^2 work) fits the
+    budget and the inputs, outputs and workspace fit the free device memory. Each
+    size is checked on two query rows against the oracle (gQ, gdO) and on the key /
+    value shift invariants: sum_j gK_j = 0 and sum_j gV_j = 0 up to rounding, here
+    at most 1e-3 of sum_j |gK_j| (|gV_j|) per head dimension."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    wu = workload.custom(1, 1, 4096, 64, "bf16", False)
+    gu = {k: v.to(dev) for k, v in workload.make_inputs(wu, args.seed).items()}
+    fb.bob_attention(*[gu[k] for k in workload.INPUT_NAMES], tau=wu.scale, causal=False)
+    torch.cuda.synchronize()
+    del gu
+    records = []
+    best = None
+    n = 262144
+    while True:
+        w = workload.custom(1, 1, n, 64, "bf16", False, name=f"probe_{n}")
+        need = (fb.workspace_bytes(1, 1, n, 64, w.torch_dtype) + 11 * n * 64 * 2) * 1.1
+        free, _ = torch.cuda.mem_get_info(dev)
+        if need > free:
+            log(f"max-n probe: N={n} needs {need / 2**30:.1f} GiB, {free / 2**30:.1f} GiB free; stop")
+            break
+        log(f"max-n probe: N={n}: generating inputs")
+        cpu_in = workload.make_inputs(w, args.seed)
+        g = {k: v.to(dev) for k, v in cpu_in.items()}
+        log(f"max-n probe: N={n}: call")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = fb.bob_attention(*[g[k] for k in workload.INPUT_NAMES], tau=w.scale, causal=False)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+        finite = all(bool(torch.isfinite(o).all()) for o in out)
+        shift = {}
+        for name, o in (("gK", out[1]), ("gV", out[2])):
+            x = o[0, 0].double()
+            shift[name] = float((x.sum(0).abs() / x.abs().sum(0).clamp_min(1e-300)).max())
+        rows = np.array([0, n - 1])
+        arrs = [workload.to_f64(cpu_in[k][0, 0]) for k in workload.INPUT_NAMES]
+        r = oracle.bob_rows_head(*arrs, w.scale, False, rows)
+        errs = {}
+        for name, o in (("gQ", out[0]), ("gdO", out[3])):
+            got = o[0, 0, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+            errs[name] = float(np.linalg.norm(got - r[name]) / np.linalg.norm(r[name]))
+        ok = finite and max(errs.values()) <= 2e-2 and max(shift.values()) <= 1e-3 and t <= args.max_n_budget
+        rec = {"N": n, "s": round(t, 3), "finite": finite, "row_rel_err": {k: round(v, 6) for k, v in errs.items()},
+               "shift_sum_rel": {k: float(f"{v:.3g}") for k, v in shift.items()}, "ok": ok}
+        log(f"max-n probe: {rec}")
+        records.append(rec)
+        del g, out, cpu_in, arrs
+        torch.cuda.empty_cache()
+        if not ok:
+            break
+        best = n
+        if 4 * t > args.max_n_budget:
+            break
+        n *= 2
+    print(json.dumps({"max_n_run": best, "budget_s": args.max_n_budget, "d": 64, "dtype": "bf16", "probe": records}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +325,11 @@ def main():
                     help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
     ap.add_argument("--schedule", choices=("two_pass", "four_pass"), default="two_pass",
                     help="four_pass times the ablation schedule (separate alpha, E and row-output sweeps)")
+    ap.add_argument("--max-n-probe", action="store_true",
+                    help="only find the largest N = 2^k >= 262144 (B = H = 1, d = 64, bf16) whose call finishes "
+                         "within --max-n-budget seconds and passes sampled oracle rows and the key/value shift "
+                         "invariants")
+    ap.add_argument("--max-n-budget", type=float, default=60.0, help="seconds per call for --max-n-probe")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
@@ -289,6 +361,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.max_n_probe:
+        max_n_probe(fb, workload, dev, args)
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
