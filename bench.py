@@ -138,8 +138,9 @@ def digest_trace(trace_dir, out, bench_log=None):
         n = r["Name"].replace("void fb::", "").split("(")[0]
         lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    lines += ["", "Calls: bench.py's 2 warm-up calls, its 5 timed calls (HIP events around pass 1 only) and 5 "
-              "repeats without any library events."]
+    lines += ["", "Calls: bench.py's 2 warm-up calls, its 5 timed calls (HIP events around pass 1 only), 5 "
+              "repeats without any library events, then the statistics call and 2 + 5 calls of the ledger path "
+              "(pass 1 and pass 2 from saved statistics)."]
     if traced:
         r = traced["roofline"]
         lines += ["", f"The traced bench.py run itself reported {traced['ms_per_step'] * 1e3:.1f} us per call and "
