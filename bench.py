@@ -152,6 +152,71 @@ def digest_trace(trace_dir, out, bench_log=None):
     print("\n".join(lines))
 
 
+SQ_COMMAND = ("rocprofv3 --pmc {counters} -d <{tag}> -o run --output-format csv -- python3 bench.py --steps 5 "
+              "--warmup 2 --no-cpu --no-endpoint --no-parity")
+KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
+
+
+def digest_sq(out, trace_dir, *runs):
+    """Matrix-core and issue counters per kernel (long_16k), from rocprofv3 --pmc
+    runs given as DIR=COUNTER,COUNTER,...: per-dispatch means, the bf16 MFMA flops
+    the hardware counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against the FLOP
+    model's units, and those flops over the kernel-trace average duration."""
+    import math as _m
+
+    w_unit = 2.0 * 64 * 16384 * 16384  # one unit at long_16k
+    vals = {}
+    cmds = []
+    for r in runs:
+        d, counters = r.split("=", 1)
+        cmds.append(SQ_COMMAND.format(counters=counters.replace(",", " "), tag=os.path.basename(d.rstrip("/"))))
+        for r2 in _csv_rows(d, "counter_collection.csv"):
+            k = r2["Kernel_Name"].replace("void fb::", "").split("(")[0]
+            vals.setdefault(k, {}).setdefault(r2["Counter_Name"], []).append(float(r2["Counter_Value"]))
+    durs = {}
+    for r in _csv_rows(trace_dir, "kernel_stats.csv"):
+        durs[r["Name"].replace("void fb::", "").split("(")[0]] = float(r["AverageNs"]) * 1e-9
+    names = sorted({c for v in vals.values() for c in v})
+    lines = ["# Matrix-core and issue counters: BoB call at long_16k (B=1, H=1, N=16384, d=64, bf16, non-causal)", "",
+             "Commands (repository root, one MI355X; one counter set per run):", "", "```"] + cmds + [
+             "python3 bench.py --digest-sq " + os.path.relpath(out, ROOT) + " <TRACE> <DIR>=<COUNTERS> ...", "```", "",
+             f"Pass-1 source hash ({' + '.join(PASS1_SOURCES)}): {pass1_source_hash()}", "",
+             "Per-dispatch means over every launch of the run (warm-up, timed and ledger-path calls).", "",
+             "| Kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k in sorted(vals):
+        lines.append(f"| `{k}` | " + " | ".join(f"{sum(vals[k].get(c, [_m.nan])) / max(1, len(vals[k].get(c, []))):.4g}"
+                                                for c in names) + " |")
+    lines += ["", "Derived. MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; model = the kernel's units x "
+              f"{w_unit:.4g} flops; trace avg = the kernel-trace average of the same command. GRBM_GUI_ACTIVE "
+              "sums the 8 XCDs, so the clock during the kernel is GRBM_GUI_ACTIVE / 8 / trace avg and the "
+              "matrix cores' busy fraction is SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs). "
+              "SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_LDS count in the same unit, so their ratios "
+              "are fractions of the waves' resident time.", "",
+              "| Kernel | MFMA flops / dispatch | counted / model | trace avg (us) | counted TFLOP/s | clock (GHz) | "
+              "MFMA busy | co-exec / MFMA busy | VALU active / wave | LDS wait / wave |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+
+    def mean(k, c):
+        v = vals[k].get(c)
+        return sum(v) / len(v) if v else _m.nan
+
+    for k in sorted(vals):
+        units = next((u for p, u in KERNEL_UNITS.items() if k.startswith(p)), None)
+        if units is None or _m.isnan(mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16")):
+            continue
+        fl = mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        t = durs.get(k, _m.nan)
+        cyc = mean(k, "GRBM_GUI_ACTIVE") / 8
+        lines.append(f"| `{k}` | {fl:.4g} | {fl / (units * w_unit):.3f} | {t * 1e6:.1f} | {fl / t / 1e12:.0f} | "
+                     f"{cyc / t / 1e9:.2f} | {mean(k, 'SQ_VALU_MFMA_BUSY_CYCLES') / (cyc * 1024):.3f} | "
+                     f"{mean(k, 'SQ_VALU_MFMA_COEXEC_CYCLES') / mean(k, 'SQ_VALU_MFMA_BUSY_CYCLES'):.3f} | "
+                     f"{mean(k, 'SQ_ACTIVE_INST_VALU') / mean(k, 'SQ_WAVE_CYCLES'):.3f} | "
+                     f"{mean(k, 'SQ_WAIT_INST_LDS') / mean(k, 'SQ_WAVE_CYCLES'):.3f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, inputs, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: query rows [0, R) of head 0 against all N keys; extrapolate by N/R."""
@@ -335,6 +400,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (csv dirs) into OUT (json)")
+    ap.add_argument("--digest-sq", nargs="+", metavar="OUT TRACE_DIR DIR=COUNTERS",
+                    help="summarise rocprofv3 --pmc runs of matrix-core / issue counters into OUT (markdown)")
     ap.add_argument("--digest-trace", nargs="+", metavar="TRACE_DIR OUT [BENCH_LOG]",
                     help="summarise a rocprofv3 --kernel-trace --stats run (csv dir) into OUT (markdown)")
     args = ap.parse_args()
@@ -343,6 +410,9 @@ def main():
         return
     if args.digest_trace:
         digest_trace(*args.digest_trace)
+        return
+    if args.digest_sq:
+        digest_sq(*args.digest_sq)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
