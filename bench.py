@@ -152,6 +152,76 @@ def digest_trace(trace_dir, out, bench_log=None):
     print("\n".join(lines))
 
 
+def ledger_terms(N, d, BH=1, br=128, bc=128, esz=2):
+    """The pages' transfer ledger (review page, Strengths, Theorem 4.3; our reading of
+    its garbled terms): Q = 12Nd + 4N + 4dN^2/B_r + (3d + 4)N^2/B_c elements per head,
+    split here by pass and priced in bytes (16-bit tensors, float32 row vectors)."""
+    p1_fixed = (4 * N * d + 2 * N * d) * esz + (2 * N + 2 * N) * 4   # Q, dO, UQ, O in; gQ, gdO out; L, D in; alpha, E out
+    p1_stream = 4 * d * N * N / br * esz                               # K, V, UK, UV per query tile
+    p2_fixed = (4 * N * d + 2 * N * d) * esz                           # K, V, UK, UV in; gK, gV out
+    p2_stream = (3 * d * esz + 4 * 4) * N * N / bc                     # Q, dO, UQ and L, D, alpha, E per key tile
+    return {"pass1": (BH * p1_fixed, BH * p1_stream), "pass2": (BH * p2_fixed, BH * p2_stream)}
+
+
+def digest_ledger(out, copy_fetch, copy_write, *runs):
+    """HBM bytes per dispatch (FETCH_SIZE x its copy factor + WRITE_SIZE x its copy
+    factor) of each kernel of one BoB call, against the transfer ledger's terms.
+    runs: WORKLOAD=FETCH_DIR,WRITE_DIR ..."""
+    import workload as _wl
+
+    copy_bytes = 512 << 20
+    cf, cw = _per_kernel_mean(copy_fetch), _per_kernel_mean(copy_write)
+    ck = [k for k in cf if "copy" in k.lower()][0]
+    ff, wf = copy_bytes / (cf[ck] * 1024), copy_bytes / (cw[ck] * 1024)
+    lines = ["# HBM bytes against the transfer ledger (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (repository root, one MI355X; one counter per run; <W> is the workload):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE -d <FETCH_W> -o run --output-format csv -- python3 bench.py --workload <W> "
+             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown",
+             "rocprofv3 --pmc WRITE_SIZE -d <WRITE_W> -o run --output-format csv -- python3 bench.py --workload <W> "
+             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown",
+             "rocprofv3 --pmc FETCH_SIZE -d <COPY_FETCH> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+             "rocprofv3 --pmc WRITE_SIZE -d <COPY_WRITE> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+             "python3 bench.py --digest-ledger " + os.path.relpath(out, ROOT) +
+             " <COPY_FETCH> <COPY_WRITE> <W>=<FETCH_W>,<WRITE_W> ...", "```", "",
+             f"Counter scale from a plain 512 MiB device copy: FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {wf:.3f}.", "",
+             "Ledger (per head, elements priced at 2 B for 16-bit tensors and 4 B for float32 row vectors, "
+             "B_r = B_c = 128, the kernels' query and key tiles): pass 1 = 4Nd + 2N in, 2Nd + 2N out, "
+             "4dN^2/B_r streamed; pass 2 = 4Nd in, 2Nd out, (3d + 4)N^2/B_c streamed. The statistics kernel "
+             "and the split merges are outside the ledger. Measured bytes below the streamed term mean the "
+             "re-streamed tiles were served by L2 / MALL, as the pages' own analysis expects of a real cache.", ""]
+    for r in runs:
+        name, dirs = r.split("=", 1)
+        fdir, wdir = dirs.split(",")
+        w = _wl.WORKLOADS[name]
+        f, wr = _per_kernel_mean(fdir), _per_kernel_mean(wdir)
+        led = ledger_terms(w.N, w.d, w.B * w.H)
+        lines += [f"## {name}: B={w.B}, H={w.H}, N={w.N}, d={w.d}, {w.dtype}, "
+                  f"{'causal' if w.causal else 'non-causal'}", "",
+                  "| Kernel | read (MB) | written (MB) | HBM total (MB) | ledger fixed (MB) | ledger streamed (MB) | "
+                  "HBM / (fixed + streamed) |", "|---|---|---|---|---|---|---|"]
+        tot = 0.0
+        for k in sorted(f):
+            short = k.replace("void fb::", "").split("(")[0]
+            rd, wb = f[k] * 1024 * ff, wr.get(k, 0.0) * 1024 * wf
+            tot += rd + wb
+            key = "pass1" if short.startswith("bob_pass1_kernel<") else "pass2" if short.startswith(
+                "bob_pass2_kernel<") else None
+            if key:
+                fx, st = led[key]
+                lines.append(f"| `{short}` | {rd / 1e6:.1f} | {wb / 1e6:.1f} | {(rd + wb) / 1e6:.1f} | {fx / 1e6:.1f} | "
+                             f"{st / 1e6:.0f} | {(rd + wb) / (fx + st):.4f} |")
+            else:
+                lines.append(f"| `{short}` | {rd / 1e6:.1f} | {wb / 1e6:.1f} | {(rd + wb) / 1e6:.1f} | — | — | — |")
+        fx = led["pass1"][0] + led["pass2"][0]
+        st = led["pass1"][1] + led["pass2"][1]
+        lines += ["", f"Per dispatch of every kernel of one call (averaged over the run's calls): {tot / 1e6:.1f} MB "
+                  f"of HBM traffic; the ledger's fixed part 12Nd + 4N is {fx / 1e6:.1f} MB and its streamed part "
+                  f"{st / 1e6:.0f} MB at B = 128.", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 SQ_COMMAND = ("rocprofv3 --pmc {counters} -d <{tag}> -o run --output-format csv -- python3 bench.py --steps 5 "
               "--warmup 2 --no-cpu --no-endpoint --no-parity")
 KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
@@ -383,7 +453,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-endpoint", action="store_true", help="skip the N=262144 feasibility call")
+    ap.add_argument("--no-endpoint", action="store_true",
+                    help="skip the N=262144 feasibility call and the timings of the other multi-head shapes")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass with HIP events around every kernel (the kernels field is then empty)")
@@ -400,6 +471,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (csv dirs) into OUT (json)")
+    ap.add_argument("--digest-ledger", nargs="+", metavar="OUT COPY_FETCH COPY_WRITE WORKLOAD=FETCH,WRITE",
+                    help="summarise FETCH_SIZE / WRITE_SIZE runs per workload against the transfer ledger (markdown)")
     ap.add_argument("--digest-sq", nargs="+", metavar="OUT TRACE_DIR DIR=COUNTERS",
                     help="summarise rocprofv3 --pmc runs of matrix-core / issue counters into OUT (markdown)")
     ap.add_argument("--digest-trace", nargs="+", metavar="TRACE_DIR OUT [BENCH_LOG]",
@@ -413,6 +486,9 @@ def main():
         return
     if args.digest_sq:
         digest_sq(*args.digest_sq)
+        return
+    if args.digest_ledger:
+        digest_ledger(*args.digest_ledger)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -492,13 +568,18 @@ def main():
     ms = total_ms / args.steps
     log(f"bench: {ms:.4f} ms/call")
 
-    # the same calls without any library events
+    # the same calls without any library events; stream events around each call give
+    # the median and the minimum
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start.record()
-    for _ in range(args.steps):
+    for e0, e1 in evs:
+        e0.record()
         step()
+        e1.record()
     stop.record()
     torch.cuda.synchronize()
     ms_clean = start.elapsed_time(stop) / args.steps
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
 
     # the ledger path: pass 1 + pass 2 from saved statistics (19 units), same inputs
     with_stats = None
@@ -555,6 +636,8 @@ def main():
         "mfma_util": round(tflops / peak, 5),
         "executed_units": UNITS["exec"] if args.schedule == "two_pass" else UNITS["four_pass_exec"],
         "ms_per_call_no_kernel_events": round(ms_clean, 5),
+        "ms_per_call_median": round(per_call[len(per_call) // 2], 5),
+        "ms_per_call_min": round(per_call[0], 5),
         "sum_of_kernel_ms_per_call": round(sum(v["avg_ms"] * v["launches"] for v in kern.values()) / args.steps, 5),
         "tflops_useful_12_units": round(UNITS["useful"] * unit / (ms * 1e-3) / 1e12, 3),
         "with_stats": with_stats,
@@ -574,6 +657,35 @@ def main():
             got = o[0, 0, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
             errs[name] = float(np.linalg.norm(got - r[name]) / np.linalg.norm(r[name]))
         result["parity_sampled_rows"] = {k: round(v, 6) for k, v in errs.items()}
+
+    if not args.no_endpoint and args.schedule == "two_pass":
+        # the other multi-head shapes, timed the same way (whole calls, inputs resident)
+        others = {}
+        for name, reps in (("gpt2_hessian", 20), ("wide_64k", 3)):
+            wo = workload.WORKLOADS[name]
+            log(f"bench: {wo.describe()}")
+            go = {k: v.to(dev) for k, v in workload.make_inputs(wo, args.seed).items()}
+            wso = torch.empty(max(1, fb.workspace_bytes(wo.B, wo.H, wo.N, wo.d, wo.torch_dtype)), dtype=torch.uint8,
+                              device=dev)
+            oo = [torch.empty_like(go["Q"]) for _ in range(4)]
+
+            def step_o():
+                fb.bob_attention(*[go[n] for n in workload.INPUT_NAMES], tau=wo.scale, causal=wo.causal,
+                                 workspace=wso, out=oo)
+
+            step_o()
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(reps):
+                step_o()
+            stop.record()
+            torch.cuda.synchronize()
+            mo = start.elapsed_time(stop) / reps
+            others[name] = {"ms_per_call": round(mo, 4), "calls": reps,
+                            "tflops_21_units": round(UNITS["exec"] * flop_unit(wo) / (mo * 1e-3) / 1e12, 2),
+                            "B": wo.B, "H": wo.H, "N": wo.N, "d": wo.d, "causal": wo.causal}
+            del go, wso, oo
+        result["other_configs"] = others
 
     if not args.no_endpoint:
         we = workload.WORKLOADS["endpoint_256k"]
