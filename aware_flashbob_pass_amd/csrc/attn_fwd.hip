@@ -59,15 +59,15 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // operands with the transposing LDS load. Declared for two waves per SIMD (the
 // register form; d = 128 then needs 188 VGPRs and no AGPRs), which hides more
 // than forming the next step's tile early did.
-// The reference maximum m of a row moves only when some row of the wave sees a
-// score more than 2^kRescaleLog2 above its own m (log2 domain): until then the
-// weights 2^(s - m) may exceed 1 by up to that factor, which float32 sums and the
-// 16-bit weight operands hold with unchanged relative precision, and the result
-// is the same because the denominator l and the accumulators share m. This skips
-// most accumulator rescales after the first steps.
-// With `nsplit` > 1 each split covers a key range and writes a record
-// (accumulators, max, partial denominators) that fwd_combine merges.
-constexpr float kRescaleLog2 = 8.f;
+// The reference maximum m of a row is not tracked per step: each step forms its
+// weights 2^(s - m) with the current m and only when some lane's sum of them
+// reaches 2^32 (or is not finite, as on a row's first step, where m is -1e30)
+// does it take the step's row maximum, rescale the sums and form the weights
+// again. Weights below 2^32 keep float32 sums and 16-bit weight operands at
+// their relative precision with ample range left, and the result is unchanged
+// because the denominator l and the accumulators share m. The maximum's tree,
+// pair exchange and compare then run only on those steps.
+constexpr float kLazyLimit = 4294967296.f;  // 2^32
 
 template <class TT, int D, bool CAUSAL, bool WITH_D>
 __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
@@ -143,27 +143,31 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
           if (!(key < N && (!CAUSAL || key <= qi))) sc[r] = -INFINITY;
         }
       }
-      float mx = max16(sc);
-      if (fold) mx *= cs;
-      mx = pair_max32(mx);
-      const float mnew = fmaxf(m, mx);
-      if (__ballot(mnew > m + kRescaleLog2)) {
+      V pp[NK];
+      float ls = 0.f;  // this step's part of the denominator
+      auto weights = [&]() {
+        ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sc[r], cm, -m));
+          ls += p;
+          vset<TT>(pp[r >> 3], r & 7, p);
+        }
+      };
+      weights();
+      if (__ballot(!(ls < kLazyLimit))) {  // rare: move m to the row maximum
+        float mx = max16(sc);
+        if (fold) mx *= cs;
+        mx = pair_max32(mx);
+        const float mnew = fmaxf(m, mx);
         const float f = fast_exp2(m - mnew);
         l *= f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] *= f;
         m = mnew;
+        weights();
       }
-      V pp[NK];
-#pragma unroll
-      for (int t = 0; t < DK; ++t) {
-#pragma unroll
-        for (int r = t * 16 / DK; r < (t + 1) * 16 / DK; ++r) {
-          const float p = fast_exp2(fmaf(sc[r], cm, -m));
-          l += p;
-          vset<TT>(pp[r >> 3], r & 7, p);
-        }
-      }
+      l += ls;
 #pragma unroll
       for (int t = 0; t < NK; ++t)
 #pragma unroll
