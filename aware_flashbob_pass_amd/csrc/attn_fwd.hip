@@ -200,32 +200,68 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
   R[MB * 16 * 64 + 64 + lane] = l;
 }
 
-// Merge the split records of each wave (fixed split order) and apply the epilogue.
+// Merge the split records of one wave (fixed split order) and apply the epilogue.
+// A workgroup takes one wave's record (grid x = query tile x wave); the 8 threads
+// 8 n .. 8 n + 7 hold row n of it: record lanes n and n + 32 (g) times slots
+// 4 r4 .. 4 r4 + 3 of every head-dim block, so the loads are 16 contiguous bytes per
+// thread, four times as many waves are in flight as with one thread per record
+// lane, and D = dO . O of the row is summed over those 8 adjacent lanes.
 template <class TT, int D, bool WITH_D>
 __global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
+  using T = typename TT::elem;
   constexpr int MB = G::MB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int g = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y;
-  const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
+  constexpr int MOFF = MB * 16 * 64;  // m[64], then l[64], after the accumulators
+  const int t = threadIdx.x, n = t >> 3, g = (t >> 2) & 1, r4 = t & 3;
+  const int L = g * 32 + n;
+  const int qt = blockIdx.x >> 2, wave = blockIdx.x & 3, bh = blockIdx.y;
+  const int N = a.N;
+  const int qi = qt * kBlockRows + wave * kTile + n;
   auto rec = [&](int sp) {
-    return a.part + ((((size_t)sp * a.BH + bh) * row_tiles(a.N) + blockIdx.x) * 4 + wave) * fwd_record_floats(D);
+    return a.part + ((((size_t)sp * a.BH + bh) * row_tiles(N) + qt) * 4 + wave) * fwd_record_floats(D);
   };
-  float M = -1e30f;
-  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, rec(sp)[MB * 16 * 64 + lane]);
-  f32x16 acc[MB];
+  float M = -1e30f;  // m is the same in record lanes n and n + 32
+  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, rec(sp)[MOFF + L]);
+  f32x4 acc[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
-  float l = 0.f;
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float llo = 0.f, lhi = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) {
     const float* R = rec(sp);
-    const float w = fast_exp2(R[MB * 16 * 64 + lane] - M);
-    l += w * R[MB * 16 * 64 + 64 + lane];
+    const float w = fast_exp2(R[MOFF + L] - M);
+    llo += w * R[MOFF + 64 + n];
+    lhi += w * R[MOFF + 96 + n];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] += w * load_acc16(R + (mb * 64 + lane) * 16);
+    for (int mb = 0; mb < MB; ++mb) acc[mb] += w * *reinterpret_cast<const f32x4*>(R + (mb * 64 + L) * 16 + r4 * 4);
   }
-  fwd_epilogue<TT, D, WITH_D>(acc, M, l, qi, g, bh, a);
+  const float lt = llo + lhi;
+  const float inv = 1.f / lt;
+  const size_t row = (size_t)bh * N + qi;
+  float dot = 0.f;
+  if (qi < N) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int dim = mb * 32 + kappa(r4 * 4, g);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[mb][e] * inv;
+      store4<TT>(reinterpret_cast<T*>(a.O) + row * D + dim, o[0], o[1], o[2], o[3]);
+      if constexpr (WITH_D) {
+        float x[4];
+        load4<TT>(reinterpret_cast<const T*>(a.dO) + row * D + dim, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot += x[e] * o[e];
+      }
+    }
+  }
+  if constexpr (WITH_D) {
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+  }
+  if (qi >= N || (t & 7) != 0) return;
+  a.L[row] = M * kLn2 + __logf(lt);
+  if constexpr (WITH_D) a.D[row] = dot;
 }
 
 // Single-buffered variant (transposed LDS copy of V); used for float32 inputs.
@@ -371,7 +407,7 @@ hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, 
 
 template <class TT, int D>
 static hipError_t launch_fc_t(const FwdArgs& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH);
+  dim3 grid(row_tiles(a.N) * 4, a.BH);  // one workgroup per wave record
   if (a.D) {
     hipLaunchKernelGGL((attn_fwd_combine_kernel<TT, D, true>), grid, dim3(kBlock), 0, s, a);
   } else {

@@ -637,54 +637,41 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   }
 }
 
-// Sum the split records of each wave in split order, then apply the epilogue.
-// Sum the split records of one 32-wide head-dim block per workgroup (grid z =
-// half x block) in split order, two splits' loads in flight at a time, and apply
-// the epilogue to that block; every block forms the same alpha_i and e0_i, and
-// block 0 writes them.
+// Sum the split records of one wave in split order and apply the epilogue. A
+// workgroup takes one wave's record and one 32-wide head-dim block (grid x = query
+// tile x wave, z = half x block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of
+// record lane t / 4, so consecutive threads read consecutive 16 bytes and four times
+// as many waves are in flight as with one thread per record lane. The sums are
+// formed in the same order as in one-lane-per-thread form (split by split, then
+// the row's lane pair), and block 0 writes the row scalars.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) {
   constexpr int MB = P1<TT, D>::MBA;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int g = lane >> 5, n = lane & 31;
+  constexpr int ACC = P1<TT, D>::ACC_FLOATS;
+  const int L = threadIdx.x >> 2, r4 = threadIdx.x & 3;
+  const int g = L >> 5, n = L & 31;
+  const int qt = blockIdx.x >> 2, wave = blockIdx.x & 3;
   const int bh = blockIdx.y, half = blockIdx.z / MB, mbl = blockIdx.z % MB;
-  const int qi = blockIdx.x * kBlockRows + wave * kTile + n;
-  f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};  // A, B, C, X of block mbl
-  float alpha_p = 0.f, e0_p = 0.f;
-  auto rec = [&](int sp) { return pass1_record<TT, D>(a, sp, bh, blockIdx.x, wave, half); };
-  int sp = 0;
-  for (; sp + 2 <= a.nsplit; sp += 2) {
-    const float* R0 = rec(sp);
-    const float* R1 = rec(sp + 1);
-    f32x16 v0[4], v1[4];
+  const int qi = qt * kBlockRows + wave * kTile + n;
+  f32x4 acc[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v0[k] = load_acc16(R0 + ((k * MB + mbl) * 64 + lane) * 16);
-      v1[k] = load_acc16(R1 + ((k * MB + mbl) * 64 + lane) * 16);
-    }
-    const float a0 = R0[P1<TT, D>::ACC_FLOATS + lane], e0 = R0[P1<TT, D>::ACC_FLOATS + 64 + lane];
-    const float a1 = R1[P1<TT, D>::ACC_FLOATS + lane], e1 = R1[P1<TT, D>::ACC_FLOATS + 64 + lane];
+  for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float alo = 0.f, ahi = 0.f, elo = 0.f, ehi = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* R = pass1_record<TT, D>(a, sp, bh, qt, wave, half);
+    f32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k] += v0[k];
-      acc[k] += v1[k];
-    }
-    alpha_p += a0;
-    alpha_p += a1;
-    e0_p += e0;
-    e0_p += e1;
+    for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(R + ((k * MB + mbl) * 64 + L) * 16 + r4 * 4);
+    alo += R[ACC + n];
+    ahi += R[ACC + 32 + n];
+    elo += R[ACC + 64 + n];
+    ehi += R[ACC + 96 + n];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += v[k];
   }
-  if (sp < a.nsplit) {
-    const float* R = rec(sp);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] += load_acc16(R + ((k * MB + mbl) * 64 + lane) * 16);
-    alpha_p += R[P1<TT, D>::ACC_FLOATS + lane];
-    e0_p += R[P1<TT, D>::ACC_FLOATS + 64 + lane];
-  }
-  const float alpha = pair_sum32(alpha_p);
-  const float e0 = pair_sum32(e0_p);
-  pass1_epilogue_block<TT, D>(acc[0], acc[1], acc[2], acc[3], alpha, e0, qi, g, bh, half * MB + mbl, a);
-  if (blockIdx.z == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
+  const float alpha = alo + ahi, e0 = elo + ehi;
+  pass1_epilogue_quad<TT, D>(acc[0], acc[1], acc[2], acc[3], alpha, e0, qi, g, bh, half * MB + mbl, r4, a);
+  if (blockIdx.z == 0 && r4 == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
 }
 
 template <class TT, int D>
@@ -726,7 +713,7 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_c1_t(const Pass1Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH, P1<TT, D>::NH * P1<TT, D>::MBA);
+  dim3 grid(row_tiles(a.N) * 4, a.BH, P1<TT, D>::NH * P1<TT, D>::MBA);  // one workgroup per wave record
   hipLaunchKernelGGL((bob_pass1_combine_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

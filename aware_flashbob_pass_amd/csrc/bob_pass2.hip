@@ -21,21 +21,27 @@
 
 namespace fb {
 
+// gK_j and gV_j at the 4 head dims of slots 4 r4 .. 4 r4 + 3 of head-dim block mb.
 template <class TT, int D>
-__device__ inline void pass2_epilogue_block(const f32x16& dK, const f32x16& dV, int kj, int g, int bh, int mb,
-                                            const Pass2Args& a) {
+__device__ inline void pass2_epilogue_quad(const f32x4& dK, const f32x4& dV, int kj, int g, int bh, int mb, int r4,
+                                           const Pass2Args& a) {
   using T = typename TT::elem;
   if (kj >= a.N) return;
   const size_t row = (size_t)bh * a.N + kj;
-  T* gK = reinterpret_cast<T*>(a.gK) + row * D;
-  T* gV = reinterpret_cast<T*>(a.gV) + row * D;
+  const int dim = mb * 32 + kappa(r4 * 4, g);
   const float tau = a.tau;
+  store4<TT>(reinterpret_cast<T*>(a.gK) + row * D + dim, tau * dK[0], tau * dK[1], tau * dK[2], tau * dK[3]);
+  store4<TT>(reinterpret_cast<T*>(a.gV) + row * D + dim, dV[0], dV[1], dV[2], dV[3]);
+}
+
+template <class TT, int D>
+__device__ inline void pass2_epilogue_block(const f32x16& dK, const f32x16& dV, int kj, int g, int bh, int mb,
+                                            const Pass2Args& a) {
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
-    const int dim = mb * 32 + kappa(r4 * 4, g);
-    const int r = r4 * 4;
-    store4<TT>(gK + dim, tau * dK[r], tau * dK[r + 1], tau * dK[r + 2], tau * dK[r + 3]);
-    store4<TT>(gV + dim, dV[r], dV[r + 1], dV[r + 2], dV[r + 3]);
+    const f32x4 k4 = {dK[r4 * 4], dK[r4 * 4 + 1], dK[r4 * 4 + 2], dK[r4 * 4 + 3]};
+    const f32x4 v4 = {dV[r4 * 4], dV[r4 * 4 + 1], dV[r4 * 4 + 2], dV[r4 * 4 + 3]};
+    pass2_epilogue_quad<TT, D>(k4, v4, kj, g, bh, mb, r4, a);
   }
 }
 
@@ -376,42 +382,29 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   pass2_write_record<TT, D>(accK, accV, split, bh, kt, wave, lane, a);
 }
 
-// Sum the split records of one 32-wide head-dim block per workgroup (grid z) in
-// split order, four splits' loads in flight at a time, and write that block.
+// Sum the split records of one wave in split order and write one 32-wide head-dim
+// block of gK, gV. A workgroup takes one wave's record and one block (grid x = key
+// tile x wave, z = block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of record
+// lane t / 4, so consecutive threads read consecutive 16 bytes and four times as
+// many waves are in flight as with one thread per record lane.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
   constexpr int MB = Geo<TT, D>::MB;
-  constexpr int U = 4;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int g = lane >> 5, n = lane & 31;
+  const int L = threadIdx.x >> 2, r4 = threadIdx.x & 3;
+  const int g = L >> 5, n = L & 31;
+  const int kt = blockIdx.x >> 2, wave = blockIdx.x & 3;
   const int bh = blockIdx.y, mb = blockIdx.z;
-  const int kj = blockIdx.x * kBlockRows + wave * kTile + n;
+  const int kj = kt * kBlockRows + wave * kTile + n;
   const int kt_count = row_tiles(a.N);
-  auto rec = [&](int sp) {
-    return a.part + ((((size_t)sp * a.BH + bh) * kt_count + blockIdx.x) * 4 + wave) * pass2_record_floats(D);
-  };
-  f32x16 dK = zero16(), dV = zero16();
-  int sp = 0;
-  for (; sp + U <= a.nsplit; sp += U) {
-    f32x16 k[U], v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float* R = rec(sp + u);
-      k[u] = load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-      v[u] = load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      dK += k[u];
-      dV += v[u];
-    }
+  f32x4 dK = {0.f, 0.f, 0.f, 0.f}, dV = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* R = a.part + ((((size_t)sp * a.BH + bh) * kt_count + kt) * 4 + wave) * pass2_record_floats(D);
+    const f32x4 k4 = *reinterpret_cast<const f32x4*>(R + ((0 * MB + mb) * 64 + L) * 16 + r4 * 4);
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(R + ((1 * MB + mb) * 64 + L) * 16 + r4 * 4);
+    dK += k4;
+    dV += v4;
   }
-  for (; sp < a.nsplit; ++sp) {
-    const float* R = rec(sp);
-    dK += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-    dV += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
-  }
-  pass2_epilogue_block<TT, D>(dK, dV, kj, g, bh, mb, a);
+  pass2_epilogue_quad<TT, D>(dK, dV, kj, g, bh, mb, r4, a);
 }
 
 template <class TT, int D>
@@ -478,7 +471,7 @@ hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_r2_t(const Pass2Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N), a.BH, Geo<TT, D>::MB);
+  dim3 grid(row_tiles(a.N) * 4, a.BH, Geo<TT, D>::MB);  // one workgroup per wave record
   hipLaunchKernelGGL((bob_pass2_reduce_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

@@ -30,34 +30,43 @@ struct P1 {
   static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
 };
 
-// gQ_i and gdO_i over the 32-wide head-dim block `mbg` from its alpha-free sums,
-// with alpha_i and e0_i already summed over the lane pair of the row.
+// gQ_i and gdO_i at the 4 head dims of slots 4 r4 .. 4 r4 + 3 of the 32-wide
+// head-dim block `mbg` from their alpha-free sums, with alpha_i and e0_i already
+// summed over the lane pair of the row.
 template <class TT, int D>
-__device__ inline void pass1_epilogue_block(const f32x16& A, const f32x16& B, const f32x16& C, const f32x16& X,
-                                            float alpha, float e0, int qi, int g, int bh, int mbg,
-                                            const Pass1Args& a) {
+__device__ inline void pass1_epilogue_quad(const f32x4& A, const f32x4& B, const f32x4& C, const f32x4& X,
+                                           float alpha, float e0, int qi, int g, int bh, int mbg, int r4,
+                                           const Pass1Args& a) {
   using T = typename TT::elem;
   const int N = a.N;
   if (qi >= N) return;
   const size_t row = (size_t)bh * N + qi;
-  const T* O = reinterpret_cast<const T*>(a.O) + row * D;
-  T* gQ = reinterpret_cast<T*>(a.gQ) + row * D;
-  T* gdO = reinterpret_cast<T*>(a.gdO) + row * D;
+  const int dim = mbg * 32 + kappa(r4 * 4, g);
   const float tau = a.tau;
+  float o[4], q[4], x[4];
+  load4<TT>(reinterpret_cast<const T*>(a.O) + row * D + dim, o);
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    const int dim = mbg * 32 + kappa(r4 * 4, g);
-    float o[4], q[4], x[4];
-    load4<TT>(O + dim, o);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r4 * 4 + e;
-      q[e] = tau * (A[r] - alpha * B[r] - e0 * C[r]);
-      x[e] = X[r] - alpha * o[e];
-    }
-    store4<TT>(gQ + dim, q[0], q[1], q[2], q[3]);
-    store4<TT>(gdO + dim, x[0], x[1], x[2], x[3]);
+  for (int e = 0; e < 4; ++e) {
+    q[e] = tau * (A[e] - alpha * B[e] - e0 * C[e]);
+    x[e] = X[e] - alpha * o[e];
   }
+  store4<TT>(reinterpret_cast<T*>(a.gQ) + row * D + dim, q[0], q[1], q[2], q[3]);
+  store4<TT>(reinterpret_cast<T*>(a.gdO) + row * D + dim, x[0], x[1], x[2], x[3]);
+}
+
+__device__ inline f32x4 quad_of(const f32x16& v, int r4) {
+  return f32x4{v[r4 * 4], v[r4 * 4 + 1], v[r4 * 4 + 2], v[r4 * 4 + 3]};
+}
+
+// The same over the whole 32-wide head-dim block `mbg` (16 slots of the lane).
+template <class TT, int D>
+__device__ inline void pass1_epilogue_block(const f32x16& A, const f32x16& B, const f32x16& C, const f32x16& X,
+                                            float alpha, float e0, int qi, int g, int bh, int mbg,
+                                            const Pass1Args& a) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+    pass1_epilogue_quad<TT, D>(quad_of(A, r4), quad_of(B, r4), quad_of(C, r4), quad_of(X, r4), alpha, e0, qi, g,
+                               bh, mbg, r4, a);
 }
 
 // alpha_i and E_i = e0_i - alpha_i D_i of the row, and for pass 2 L_i log2(e) and
