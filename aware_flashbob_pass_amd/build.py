@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashbob.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "bob_pass1.hip", "bob_pass1_causal_d64.hip", "bob_pass2.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "bob_pass1.hip", "bob_pass1_vgpr.hip", "bob_pass2.hip", "attn_bwd.hip", "api.cpp"]
 
 # Packed fp32 VALU ops are disabled: the kernels are written with scalar fp32
 # element-wise math and must not be auto-vectorised into v_pk_* forms.
@@ -35,10 +35,10 @@ COMMON_FLAGS = [
 # instruction in front of each v_max, which is about 16 VALU instructions per
 # 32-key step. Maxima of finite values are exact either way, and nothing in that
 # file tests for NaN (api.cpp does, for its argument checks, and keeps them).
-# The causal d = 64 two-pass sweep of pass 1 takes the matrix-core VGPR form for its
-# score products (its accumulators are AGPR inline assembly); the flag applies to its
-# whole file, which holds nothing else.
-EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_causal_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The causal d = 64 and the d = 128 two-pass sweeps of pass 1 take the matrix-core
+# VGPR form for their score products (their accumulators are AGPR inline assembly);
+# the flag applies to their whole file, which holds nothing else.
+EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -1,7 +1,7 @@
 // The staged pass-1 kernel template (16-bit inputs) and its four-pass modes.
-// Included by bob_pass1.hip (every instance but the causal d = 64 two-pass one) and
-// by bob_pass1_causal_d64.hip (the causal d = 64 two-pass instances, built with the
-// matrix-core VGPR form: see that file).
+// Included by bob_pass1.hip (every instance but the VGPR-form ones) and by
+// bob_pass1_vgpr.hip (the causal d = 64 and the d = 128 two-pass instances, built with
+// the matrix-core VGPR form: see that file).
 #pragma once
 
 #include <type_traits>
@@ -12,10 +12,10 @@
 
 namespace fb {
 
-// Accumulating product into AGPRs, issued from inline assembly: used by the causal
-// d = 64 two-pass sweep, whose score products take the VGPR form
-// (bob_pass1_causal_d64.hip), so the four accumulator tiles stay in AGPRs and the
-// score tiles in VGPRs with no copies between the two files. The compiler does not see these as matrix-core
+// Accumulating product into AGPRs, issued from inline assembly: used by the two-pass
+// sweeps whose score products take the VGPR form (bob_pass1_vgpr.hip), so the four
+// accumulator tiles stay in AGPRs and the score tiles in VGPRs with no copies
+// between the two files. The compiler does not see these as matrix-core
 // ops, so the asm covers the hazards it would otherwise handle: s_nop 1 (2 wait
 // states) after the vector instruction that wrote a weight operand; reads of the
 // accumulators after the sweep wait in pass1_acc_settle.
@@ -179,12 +179,13 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   // d = 128 has no room for them next to 256 accumulator registers and forms
   // each step's score tiles at the start of the step instead.
   constexpr bool PIPE = D == 64 && MODE == kTwoPass;
-  // The causal d = 64 sweep keeps its accumulators in AGPRs from inline assembly and
-  // is compiled with the VGPR form for everything else (bob_pass1_causal_d64.hip):
-  // it then fits 246 VGPRs with no spills. The non-causal build of the same code
-  // needs more than 256 VGPRs in that form and spills ~50 values per step, which
-  // costs more than the 64 score-tile copies per step of the default form it uses.
-  constexpr bool ASM_ACC = PIPE && CAUSAL;
+  // The causal d = 64 sweep and the d = 128 sweeps keep their accumulators in AGPRs
+  // from inline assembly and are compiled with the VGPR form for everything else
+  // (bob_pass1_vgpr.hip). The non-causal d = 64 build of the same code would need more
+  // than 256 VGPRs in that form (it also holds the next step's score tiles) and spills
+  // ~50 values per step, which costs more than the 64 score-tile copies per step of the
+  // default form it keeps.
+  constexpr bool ASM_ACC = (PIPE && CAUSAL) || (D == 128 && MODE == kTwoPass);
   constexpr bool TWO = MODE == kTwoPass;
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
   constexpr bool NEED_G = MODE != kDqPass;      // the first backward needs S and dP only
