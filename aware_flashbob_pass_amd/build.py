@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashbob.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "bob_pass1.hip", "bob_pass1_vgpr.hip", "bob_pass2.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "bob_pass1.hip", "bob_pass1_vgpr.hip", "bob_pass2.hip", "bob_pass2_vgpr.hip", "attn_bwd.hip", "api.cpp"]
 
 # Packed fp32 VALU ops are disabled: the kernels are written with scalar fp32
 # element-wise math and must not be auto-vectorised into v_pk_* forms.
@@ -38,7 +38,8 @@ COMMON_FLAGS = [
 # The causal d = 64 and the d = 128 two-pass sweeps of pass 1 take the matrix-core
 # VGPR form for their score products (their accumulators are AGPR inline assembly);
 # the flag applies to their whole file, which holds nothing else.
-EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "bob_pass2_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

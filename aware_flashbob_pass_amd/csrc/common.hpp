@@ -22,6 +22,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
 #include <utility>
 #include <stdint.h>
 
@@ -321,6 +322,31 @@ __device__ inline typename TT::vec lds_tr_op(const typename TT::elem* rowbuf, in
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename TT::vec, v);
+}
+
+// Accumulating product into AGPRs, issued from inline assembly: used by the sweeps
+// compiled with the matrix-core VGPR form (bob_pass1_vgpr.hip, bob_pass2_vgpr.hip),
+// so their accumulator tiles stay in AGPRs and their score tiles in VGPRs with no
+// copies between the two files. The compiler does not see these as matrix-core ops,
+// so the asm covers the hazards it would otherwise handle: s_nop 1 (2 wait states)
+// after the vector instruction that wrote a weight operand; reads of the
+// accumulators after the sweep wait in acc_settle.
+template <class TT>
+__device__ inline void mfma_acc(f32x16& acc, typename TT::vec a, typename TT::vec b) {
+  if constexpr (std::is_same_v<TT, BF16>)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// 24 wait states after the last accumulating product before anything reads the
+// accumulator tiles (a 16-pass product's result needs 18); the operands tie every
+// later read of the tiles to this point.
+template <int MB>
+__device__ inline void acc_settle(f32x16 (&A)[MB], f32x16 (&B)[MB]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(A[mb]), "+a"(B[mb]));
 }
 
 // Index of the calling wave in its workgroup as a wave-uniform (scalar)

@@ -94,6 +94,8 @@ __host__ __device__ inline size_t fourpass_record_floats(int d) { return (size_t
 // 16-bit pass 2 at d = 64 is built for two waves per SIMD (two workgroups per CU).
 inline int pass2_blocks_per_cu(DT dt, int d) { return (dt != DT::F32 && d == 64) ? 2 : 1; }
 hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream_t s);
+// The non-causal d = 128 BoB sweep of pass 2, 16-bit inputs (VGPR form, its own translation unit).
+hipError_t launch_pass2_d128(const Pass2Args& a, DT dt, hipStream_t s);
 hipError_t launch_pass2_reduce(const Pass2Args& a, DT dt, int d, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& a, DT dt, int d, int BH, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);

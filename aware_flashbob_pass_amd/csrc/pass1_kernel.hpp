@@ -12,29 +12,12 @@
 
 namespace fb {
 
-// Accumulating product into AGPRs, issued from inline assembly: used by the two-pass
-// sweeps whose score products take the VGPR form (bob_pass1_vgpr.hip), so the four
-// accumulator tiles stay in AGPRs and the score tiles in VGPRs with no copies
-// between the two files. The compiler does not see these as matrix-core
-// ops, so the asm covers the hazards it would otherwise handle: s_nop 1 (2 wait
-// states) after the vector instruction that wrote a weight operand; reads of the
-// accumulators after the sweep wait in pass1_acc_settle.
-template <class TT>
-__device__ inline void mfma_acc(f32x16& acc, typename TT::vec a, typename TT::vec b) {
-  if constexpr (std::is_same_v<TT, BF16>)
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// 24 wait states after the last accumulating product before anything reads the
-// accumulator tiles (a 16-pass product's result needs 18); the operands tie every
-// later read of the tiles to this point.
+// 24 wait states after the last accumulating product before anything reads the four
+// accumulator tiles (see acc_settle in common.hpp).
 template <int MB>
 __device__ inline void pass1_acc_settle(f32x16 (&A)[MB], f32x16 (&B)[MB], f32x16 (&C)[MB], f32x16 (&X)[MB]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(A[mb]), "+a"(B[mb]), "+a"(C[mb]), "+a"(X[mb]));
+  acc_settle<MB>(A, B);
+  acc_settle<MB>(C, X);
 }
 
 // ---- four-pass ablation schedule (modes of the pipelined kernel) -----------------
