@@ -35,9 +35,9 @@ COMMON_FLAGS = [
 # instruction in front of each v_max, which is about 16 VALU instructions per
 # 32-key step. Maxima of finite values are exact either way, and nothing in that
 # file tests for NaN (api.cpp does, for its argument checks, and keeps them).
-# The causal d = 64 and the d = 128 two-pass sweeps of pass 1 take the matrix-core
-# VGPR form for their score products (their accumulators are AGPR inline assembly);
-# the flag applies to their whole file, which holds nothing else.
+# The two-pass sweeps of pass 1 (16-bit) and the non-causal d = 128 sweep of pass 2
+# take the matrix-core VGPR form for their score products (their accumulators are
+# AGPR inline assembly); the flag applies to their whole files, which hold nothing else.
 EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "bob_pass2_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

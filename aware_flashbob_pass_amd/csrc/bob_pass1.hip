@@ -234,8 +234,8 @@ static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
     hipError_t e = ensure_lds(&bob_pass1_simple_kernel<TT, D, CAUSAL>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bob_pass1_simple_kernel<TT, D, CAUSAL>), grid, dim3(kBlock), lds, s, a);
-  } else if constexpr (D == 64 && CAUSAL) {
-    return launch_pass1_causal_d64(a, std::is_same_v<TT, BF16> ? DT::BF16 : DT::F16, s);
+  } else if constexpr (D == 64) {
+    return launch_pass1_d64(a, std::is_same_v<TT, BF16> ? DT::BF16 : DT::F16, CAUSAL, s);
   } else if constexpr (D == 128) {
     return launch_pass1_d128(a, std::is_same_v<TT, BF16> ? DT::BF16 : DT::F16, CAUSAL, s);
   } else {

@@ -1,30 +1,27 @@
-// The pass-1 sweeps that take the matrix-core VGPR form, in a translation unit of
-// their own compiled with -mllvm -amdgpu-mfma-vgpr-form: the causal d = 64 two-pass
-// sweep and the d = 128 two-pass sweep (16-bit inputs). Their score products write
-// VGPRs that the element-wise work reads directly, while the four accumulator tiles
-// stay in AGPRs through inline-assembly products (mfma_acc). With the default form a
-// kernel of more than 256 registers puts every product in AGPRs, and each step then
-// copies its four score tiles out with v_accvgpr_read before the element-wise work.
-// The non-causal d = 64 sweep keeps that default form (bob_pass1.hip): it also holds
-// the next step's score tiles, and in this form it would need more than 256 VGPRs.
+// The two-pass sweeps of pass 1 for 16-bit inputs (d = 64 and 128), in a translation
+// unit of their own compiled with -mllvm -amdgpu-mfma-vgpr-form: their score products
+// write VGPRs that the element-wise work reads directly, while the four accumulator
+// tiles stay in AGPRs through inline-assembly products (mfma_acc). With the default
+// form a kernel of more than 256 registers puts every product in AGPRs, and each step
+// then copies its four score tiles out with v_accvgpr_read before the element-wise work.
 #include "pass1_kernel.hpp"
 
 namespace fb {
 
-template <class TT>
-static hipError_t launch_t(const Pass1Args& a, hipStream_t s) {
+template <class TT, bool CAUSAL>
+static hipError_t launch_64(const Pass1Args& a, hipStream_t s) {
   const size_t lds = pass1_lds_bytes<TT, 64>();
-  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, true, kTwoPass>, lds);
+  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, true, kTwoPass>), dim3(row_tiles(a.N), a.BH, a.nsplit), dim3(kBlock),
+  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass>), dim3(row_tiles(a.N), a.BH, a.nsplit), dim3(kBlock),
                      lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_pass1_causal_d64(const Pass1Args& a, DT dt, hipStream_t s) {
+hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s) {
   switch (dt) {
-    case DT::BF16: return launch_t<BF16>(a, s);
-    case DT::F16: return launch_t<F16>(a, s);
+    case DT::BF16: return causal ? launch_64<BF16, true>(a, s) : launch_64<BF16, false>(a, s);
+    case DT::F16: return causal ? launch_64<F16, true>(a, s) : launch_64<F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -76,9 +76,9 @@ inline hipError_t ensure_lds(K* kernel, size_t bytes) {
 hipError_t launch_attn_fwd(const FwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
 hipError_t launch_attn_fwd_combine(const FwdArgs& a, DT dt, int d, hipStream_t s);
 hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream_t s);
-// The VGPR-form two-pass sweeps of 16-bit inputs, causal d = 64 and d = 128 (their own
+// The two-pass sweeps of 16-bit inputs, d = 64 and d = 128 (VGPR form, their own
 // translation unit; called by launch_pass1).
-hipError_t launch_pass1_causal_d64(const Pass1Args& a, DT dt, hipStream_t s);
+hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_d128(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
 // Four-pass ablation schedule, 16-bit inputs: sweep 0 writes alpha, sweep 1 E

@@ -1,7 +1,7 @@
 // The staged pass-1 kernel template (16-bit inputs) and its four-pass modes.
-// Included by bob_pass1.hip (every instance but the VGPR-form ones) and by
-// bob_pass1_vgpr.hip (the causal d = 64 and the d = 128 two-pass instances, built with
-// the matrix-core VGPR form: see that file).
+// Included by bob_pass1.hip (the four-pass modes and the first backward's dQ sweep) and
+// by bob_pass1_vgpr.hip (the two-pass instances, built with the matrix-core VGPR form:
+// see that file).
 #pragma once
 
 #include <type_traits>
@@ -140,8 +140,8 @@ __device__ inline void pass1_schedule() {
 // kEnergyPass sweeps again for E with alpha known, and kRowsPass forms
 // gQ = tau (dS UK + Sbar K) and gdO = P UV + dPbar V with alpha and E known.
 // Waves per SIMD each pass-1 kernel is built for: the two-pass kernel keeps four
-// float32 accumulator tiles plus the next step's score tiles (one wave, AGPR
-// accumulators); the other modes hold at most two accumulator tiles, or at
+// float32 accumulator tiles in AGPRs beside its score tiles in VGPRs (one wave); the
+// other modes hold at most two accumulator tiles, or at
 // d = 128 at most the alpha sweep's score tiles, and take the register form at two.
 __host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
   return (mode == kTwoPass || (d == 128 && mode != kAlphaPass)) ? 1 : 2;
@@ -158,17 +158,17 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   // unroll) keeps three stages, two steps ahead, compiler-visible copies.
   constexpr bool DEEP = D == 64;
   constexpr int NT = 4, NBUF = DEEP ? 4 : 3, AHEAD = NBUF - 1;
-  // d = 64 keeps the next step's score tiles in registers (software pipelining);
-  // d = 128 has no room for them next to 256 accumulator registers and forms
-  // each step's score tiles at the start of the step instead.
-  constexpr bool PIPE = D == 64 && MODE == kTwoPass;
-  // The causal d = 64 sweep and the d = 128 sweeps keep their accumulators in AGPRs
-  // from inline assembly and are compiled with the VGPR form for everything else
-  // (bob_pass1_vgpr.hip). The non-causal d = 64 build of the same code would need more
-  // than 256 VGPRs in that form (it also holds the next step's score tiles) and spills
-  // ~50 values per step, which costs more than the 64 score-tile copies per step of the
-  // default form it keeps.
-  constexpr bool ASM_ACC = (PIPE && CAUSAL) || (D == 128 && MODE == kTwoPass);
+  // The two-pass sweeps keep their four accumulator tiles in AGPRs from inline
+  // assembly and are compiled with the VGPR form for everything else
+  // (bob_pass1_vgpr.hip), so the element-wise work reads the score tiles where the
+  // matrix cores wrote them. The causal d = 64 sweep also forms the next step's score
+  // tiles during the current step (software pipelining: 246 VGPRs). The non-causal
+  // d = 64 build of that pipelined form needs more than 256 VGPRs and spills ~50 values
+  // per step, so it forms each step's tiles at the start of the step like d = 128,
+  // which has no room for them either (measured faster than the pipelined sweep in the
+  // default form, whose 64 score-tile copies per step it avoids).
+  constexpr bool PIPE = D == 64 && MODE == kTwoPass && CAUSAL;
+  constexpr bool ASM_ACC = MODE == kTwoPass;
   constexpr bool TWO = MODE == kTwoPass;
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
   constexpr bool NEED_G = MODE != kDqPass;      // the first backward needs S and dP only

@@ -31,7 +31,7 @@ METRIC = "BoB ms/call + TFLOP/s (MFMA util) at N=16K,d=64 bf16; max N on 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12, "four_pass_exec": 27}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
-PASS1_SOURCES = ("bob_pass1.hip", "pass1_kernel.hpp", "pass1_common.hpp", "common.hpp", "kernels.hpp")
+PASS1_SOURCES = ("bob_pass1_vgpr.hip", "pass1_kernel.hpp", "pass1_common.hpp", "common.hpp", "kernels.hpp")
 
 
 def flop_unit(w):
