@@ -19,6 +19,10 @@
 // tiles (the whole key range, or one of `nsplit` parts of it). With splits,
 // each wave writes its raw accumulators and row partial sums as a record and
 // a combine kernel sums the records in split order and applies the epilogue.
+//
+// This file holds the float32 kernel, the split merges, the four-pass modes and
+// the launches; the staged 16-bit kernel template is in pass1_kernel.hpp and its
+// two-pass instances are built in bob_pass1_vgpr.hip.
 #include <type_traits>
 
 #include "common.hpp"

@@ -14,6 +14,10 @@
 // Q, dO, UQ (row-major and transposed copies) and the four row scalars
 // through LDS. With splits of the query range, each wave writes raw
 // accumulators and a reduce kernel sums them in split order.
+//
+// This file holds the float32 kernel, the split reduce and the launches; the
+// staged 16-bit kernel template is in pass2_kernel.hpp (its non-causal d = 128 BoB
+// instances are built in bob_pass2_vgpr.hip).
 #include <type_traits>
 
 #include "common.hpp"
@@ -21,6 +25,7 @@
 #include "pass2_kernel.hpp"
 
 namespace fb {
+
 // Single-buffered variant (transposed LDS copies); used for float32 inputs.
 template <class TT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
