@@ -1,0 +1,53 @@
+"""Host-side logic of bench.py (no GPU): the FLOP model, the transfer-ledger terms
+the HBM summaries are compared with, and the one-GPU guard."""
+
+import os
+import subprocess
+import sys
+
+import bench
+import workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_flop_unit_counts_key_query_pairs():
+    w = workload.custom(2, 3, 100, 64, "bf16", False)
+    assert bench.flop_unit(w) == 2.0 * 2 * 3 * 64 * 100 * 100
+    wc = workload.custom(2, 3, 100, 64, "bf16", True)
+    assert bench.flop_unit(wc) == 2.0 * 2 * 3 * 64 * (100 * 101 // 2)
+    assert bench.UNITS["exec"] == bench.UNITS["stats"] + bench.UNITS["pass1"] + bench.UNITS["pass2"]
+    assert bench.UNITS["two_pass"] == bench.UNITS["pass1"] + bench.UNITS["pass2"]
+
+
+def test_ledger_fixed_terms_are_12Nd_plus_4N():
+    """Review page, Strengths (Theorem 4.3): the fixed part is 12Nd + 4N elements per
+    head; 16-bit tensors at 2 bytes, float32 row vectors at 4 bytes."""
+    for N, d in ((1000, 64), (16384, 64), (65536, 128)):
+        led = bench.ledger_terms(N, d)
+        fixed = led["pass1"][0] + led["pass2"][0]
+        assert fixed == 12 * N * d * 2 + 4 * N * 4
+        # pass 1 reads Q, dO, UQ, O and L, D; writes gQ, gdO and alpha, E
+        assert led["pass1"][0] == 6 * N * d * 2 + 4 * N * 4
+        assert led["pass2"][0] == 6 * N * d * 2
+
+
+def test_ledger_streamed_terms():
+    """4dN^2/B_r (K, V, UK, UV per query tile) and (3d + 4)N^2/B_c (Q, dO, UQ and four
+    row scalars per key tile), with the tiles of the kernels (128) unless given."""
+    N, d = 16384, 64
+    led = bench.ledger_terms(N, d)
+    assert led["pass1"][1] == 4 * d * N * N / 128 * 2
+    assert led["pass2"][1] == (3 * d * 2 + 4 * 4) * N * N / 128
+    led64 = bench.ledger_terms(N, d, br=64, bc=64)
+    assert led64["pass1"][1] == 2 * led["pass1"][1]
+    assert led64["pass2"][1] == 2 * led["pass2"][1]
+    two = bench.ledger_terms(N, d, BH=2)
+    assert two["pass1"] == (2 * led["pass1"][0], 2 * led["pass1"][1])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
