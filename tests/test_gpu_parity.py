@@ -113,6 +113,15 @@ def test_bob_splits(splits, causal):
     _check_full(workload.custom(1, 2, 1000, 64, "bf16", causal), splits=splits)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("splits", [(2, 3), (7, 5)])
+def test_bob_splits_d128(splits, dtype, causal):
+    """d = 128 (pass 1 accumulates head-dim halves; the two-pass sweeps keep their
+    accumulators in AGPRs from inline assembly) through split records and merges."""
+    _check_full(workload.custom(1, 2, 900, 128, dtype, causal), splits=splits)
+
+
 def test_bob_splits_fp32_tight():
     # fp32 path with several splits stays at the fp32 bar
     _check_full(workload.custom(1, 1, 700, 64, "fp32", True), splits=(3, 4))
