@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     load_library,
     profile_start,
     profile_stop,
+    set_alloc_limit,
     set_tuning,
     workspace_bytes,
 )

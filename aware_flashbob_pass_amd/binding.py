@@ -36,6 +36,7 @@ SIGNATURES = {
     "attn_fwd": (_I, [_P] * 4 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 3 + [_P]),
     "attn_bwd": (_I, [_P] * 6 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "fb_set_tuning": (_I, [_I, _I]),
+    "fb_set_alloc_limit": (_I, [_S]),
     "fb_profile_start": (None, [ctypes.c_char_p]),
     "fb_profile_stop": (_I, [ctypes.POINTER(KernelTime), _I]),
 }
@@ -114,6 +115,11 @@ def workspace_bytes(B, H, N, d, dtype):
 
 def set_tuning(pass1_splits=0, pass2_splits=0):
     _check(load_library().fb_set_tuning(int(pass1_splits), int(pass2_splits)))
+
+
+def set_alloc_limit(nbytes=0):
+    """Cap on each device allocation the library makes itself (0: no cap)."""
+    _check(load_library().fb_set_alloc_limit(int(nbytes)))
 
 
 def bob_attention(q, k, v, do, uq, uk, uv, tau=None, causal=False, workspace=None, out=None):

@@ -33,8 +33,10 @@ COMMON_FLAGS = [
 # Per-source extra flags. The statistics kernels are compiled without NaN
 # semantics: their running row maxima then need no quieting (canonicalising)
 # instruction in front of each v_max, which is about 16 VALU instructions per
-# 32-key step. Maxima of finite values are exact either way, and nothing in that
-# file tests for NaN (api.cpp does, for its argument checks, and keeps them).
+# 32-key step. Maxima of finite values are exact either way. The one test for a
+# non-finite value in that file (the lazy rescale trigger) compares bit patterns
+# as integers, which that flag does not touch; api.cpp checks its arguments with
+# NaN semantics intact. Inputs are assumed finite.
 # The two-pass sweeps of pass 1 (16-bit) and the non-causal d = 128 sweep of pass 2
 # take the matrix-core VGPR form for their score products (their accumulators are
 # AGPR inline assembly); the flag applies to their whole files, which hold nothing else.

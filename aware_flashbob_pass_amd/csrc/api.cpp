@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -65,6 +66,32 @@ void splits_for(int BH, int N, fb::DT dt, int d, int* s0, int* s1, int* s2) {
   *s0 = g_split1 > 0 ? g_split1 : auto_splits(BH, N, 2 * kTargetBlocks);
 }
 
+// ---- library allocations -------------------------------------------------------
+std::atomic<size_t> g_alloc_limit{0};  // 0: no cap
+
+// Stream-ordered device allocation for the entry points that allocate. Refused
+// with FB_ERR_OOM, before any HIP call, when `bytes` exceeds the caller's cap
+// (fb_set_alloc_limit); then when it exceeds the free memory of the current
+// device; then when hipMallocAsync itself fails.
+fb_status_t device_alloc(void** p, size_t bytes, hipStream_t s, const char* what) {
+  *p = nullptr;
+  const size_t cap = g_alloc_limit.load();
+  if (cap && bytes > cap)
+    return fail(FB_ERR_OOM, "%s of %zu bytes exceeds the allocation limit of %zu bytes", what, bytes, cap);
+  size_t free_b = 0, total_b = 0;
+  hipError_t e = hipMemGetInfo(&free_b, &total_b);
+  if (e != hipSuccess) return fail(FB_ERR_HIP, "hipMemGetInfo: %s", hipGetErrorString(e));
+  if (bytes > free_b)
+    return fail(FB_ERR_OOM, "%s of %zu bytes exceeds the %zu bytes free on the device", what, bytes, free_b);
+  e = hipMallocAsync(p, bytes, s);
+  if (e != hipSuccess || !*p) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(FB_ERR_OOM, "%s of %zu bytes failed: %s", what, bytes, hipGetErrorString(e));
+  }
+  return FB_OK;
+}
+
 // ---- kernel timing ------------------------------------------------------------
 struct ProfRec {
   std::string name;
@@ -94,6 +121,8 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 }
 
 // ---- argument checks -----------------------------------------------------------
+constexpr int kMaxRows = 2147483647 - 255;  // B*H*N bound (see check_shape)
+
 size_t esize(fb_dtype_t dt) { return dt == FB_F32 ? 4 : 2; }
 
 fb_status_t check_shape(int B, int H, int N, int d, fb_dtype_t dtype, float tau) {
@@ -101,6 +130,12 @@ fb_status_t check_shape(int B, int H, int N, int d, fb_dtype_t dtype, float tau)
   if (d != 64 && d != 128) return fail(FB_ERR_HEADDIM, "head dim d=%d not supported (64 or 128)", d);
   if (B < 1 || H < 1 || N < 1) return fail(FB_ERR_SHAPE, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
   if ((long long)B * H > 65535) return fail(FB_ERR_SHAPE, "B*H=%lld exceeds 65535", (long long)B * H);
+  // Rows of all heads are indexed with int arithmetic in the kernels and grids
+  // (row_tiles(N) = (N + 127) / 128, resident row q0 + 31 < N + 128, launch ids
+  // tile + tiles * head): bounding B*H*N by INT_MAX keeps every one of them in
+  // range and the workspace size far inside size_t.
+  if ((long long)B * H * N > (long long)kMaxRows)
+    return fail(FB_ERR_SHAPE, "B*H*N=%lld exceeds %d", (long long)B * H * N, kMaxRows);
   if (!std::isfinite(tau)) return fail(FB_ERR_ARG, "tau must be finite");
   return FB_OK;
 }
@@ -268,6 +303,11 @@ fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits) {
   return ok();
 }
 
+fb_status_t fb_set_alloc_limit(size_t bytes) {
+  g_alloc_limit.store(bytes);
+  return ok();
+}
+
 size_t bob_workspace_bytes(int B, int H, int N, int d, fb_dtype_t dtype) {
   if (check_shape(B, H, N, d, dtype, 1.f) != FB_OK) return 0;
   return layout(B, H, N, d, dtype).total;
@@ -345,13 +385,16 @@ fb_status_t bob_attention(const void* Q, const void* K, const void* V, const voi
                           void* gQ, void* gK, void* gV, void* gdO, hipStream_t stream) {
   fb_status_t st = check_shape(B, H, N, d, dtype, tau);
   if (st) return st;
+  st = check_ptrs({{"Q", Q}, {"K", K}, {"V", V}, {"dO", dO}, {"UQ", UQ}, {"UK", UK}, {"UV", UV},
+                   {"gQ", gQ}, {"gK", gK}, {"gV", gV}, {"gdO", gdO}}, 16);
+  if (st) return st;
+  st = check_no_alias({{"gQ", gQ}, {"gK", gK}, {"gV", gV}, {"gdO", gdO}},
+                      {{"Q", Q}, {"K", K}, {"V", V}, {"dO", dO}, {"UQ", UQ}, {"UK", UK}, {"UV", UV}});
+  if (st) return st;
   const size_t bytes = layout(B, H, N, d, dtype).total;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return fail(FB_ERR_OOM, "workspace allocation of %zu bytes failed: %s", bytes, hipGetErrorString(e));
-  }
+  st = device_alloc(&ws, bytes, stream, "workspace allocation");
+  if (st) return st;
   st = bob_attention_ws(Q, K, V, dO, UQ, UK, UV, tau, causal, B, H, N, d, dtype, gQ, gK, gV, gdO, ws, bytes, stream);
   std::string msg = g_err;
   hipError_t ef = hipFreeAsync(ws, stream);
@@ -443,11 +486,8 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   const size_t d_bytes = D_out ? 0 : align256((size_t)BH * N * sizeof(float));
   void* tmp = nullptr;
   if (d_bytes + rec_bytes) {
-    hipError_t e = hipMallocAsync(&tmp, d_bytes + rec_bytes, stream);
-    if (e != hipSuccess || !tmp) {
-      (void)hipGetLastError();
-      return fail(FB_ERR_OOM, "scratch allocation of %zu bytes failed", d_bytes + rec_bytes);
-    }
+    st = device_alloc(&tmp, d_bytes + rec_bytes, stream, "scratch allocation");
+    if (st) return st;
   }
   float* D = D_out ? D_out : static_cast<float*>(tmp);
   float* part = reinterpret_cast<float*>(static_cast<char*>(tmp) + d_bytes);

@@ -61,13 +61,25 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // than forming the next step's tile early did.
 // The reference maximum m of a row is not tracked per step: each step forms its
 // weights 2^(s - m) with the current m and only when some lane's sum of them
-// reaches 2^32 (or is not finite, as on a row's first step, where m is -1e30)
-// does it take the step's row maximum, rescale the sums and form the weights
-// again. Weights below 2^32 keep float32 sums and 16-bit weight operands at
-// their relative precision with ample range left, and the result is unchanged
-// because the denominator l and the accumulators share m. The maximum's tree,
-// pair exchange and compare then run only on those steps.
-constexpr float kLazyLimit = 4294967296.f;  // 2^32
+// reaches lazy_limit (or is not finite, as on a row's first step, where m is
+// -1e30) does it take the step's row maximum, rescale the sums and form the
+// weights again. The result is unchanged because the denominator l and the
+// accumulators share m, and the maximum's tree, pair exchange and compare run
+// only on those steps. Every weight of a step that is not redone is at most its
+// lane's sum, so the limit bounds the weight operands: bf16 has the float32
+// exponent range and takes 2^32; fp16 operands must stay below 65504, its
+// largest finite value, and take 2^15. After a redo every weight is at most 1.
+template <class TT>
+__device__ constexpr float lazy_limit() {
+  return std::is_same_v<TT, F16> ? 32768.f : 4294967296.f;  // 2^15 : 2^32
+}
+
+// True when the step sum x reached `limit` or is not finite. The sum of
+// exponentials is never negative, so its bit pattern orders like its value,
+// and +inf and every NaN pattern (either sign) compare above any finite limit.
+// An integer compare keeps this exact under -fno-honor-nans, which lets the
+// compiler assume a float compare never sees a NaN.
+__device__ inline bool lazy_redo(float x, float limit) { return __float_as_uint(x) >= __float_as_uint(limit); }
 
 template <class TT, int D, bool CAUSAL, bool WITH_D>
 __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
         }
       };
       weights();
-      if (__ballot(!(ls < kLazyLimit))) {  // rare: move m to the row maximum
+      if (__ballot(lazy_redo(ls, lazy_limit<TT>()))) {  // rare: move m to the row maximum
         float mx = max16(sc);
         if (fold) mx *= cs;
         mx = pair_max32(mx);

@@ -26,7 +26,8 @@
  *    owned by the caller. Row vectors (L, D, alpha, E) are contiguous
  *    [B][H][N] float32 arrays in device memory. L is the natural-log LSE of
  *    row i of tau Q K^T.
- *  - d must be 64 or 128; B, H, N >= 1; tau finite. `causal` != 0 masks key j
+ *  - d must be 64 or 128; B, H, N >= 1; B*H <= 65535 and B*H*N <= 2^31 - 256
+ *    (else FB_ERR_SHAPE); tau finite. `causal` != 0 masks key j
  *    for query i when j > i (square, top-left aligned).
  *  - Outputs are fully overwritten (never accumulated), are written in `dtype`
  *    (round to nearest even from float32 accumulators), and must not alias any
@@ -55,7 +56,7 @@ typedef enum { FB_F32 = 0, FB_F16 = 1, FB_BF16 = 2 } fb_dtype_t;
 typedef enum {
   FB_OK = 0,
   FB_ERR_NULL = -1,      /* a required pointer is NULL                      */
-  FB_ERR_SHAPE = -2,     /* B, H or N < 1, or sizes overflow                 */
+  FB_ERR_SHAPE = -2,     /* B, H or N < 1, B*H > 65535 or B*H*N > 2^31-256  */
   FB_ERR_DTYPE = -3,     /* unknown dtype                                    */
   FB_ERR_HEADDIM = -4,   /* d not in {64, 128}                               */
   FB_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required          */
@@ -73,7 +74,9 @@ const char* fb_last_error(void);
  * In:  Q, K, V, dO, UQ, UK, UV  [B][H][N][d] dtype, device.
  * Out: gQ, gK, gV, gdO          [B][H][N][d] dtype, device, overwritten.
  * Allocates its workspace with hipMallocAsync on `stream` and frees it with
- * hipFreeAsync on the same stream; returns FB_ERR_OOM if that fails.
+ * hipFreeAsync on the same stream. Returns FB_ERR_OOM, with nothing launched,
+ * when the workspace exceeds the limit set by fb_set_alloc_limit or the free
+ * memory of the current device, or when hipMallocAsync fails.
  */
 fb_status_t bob_attention(const void* Q, const void* K, const void* V, const void* dO,
                           const void* UQ, const void* UK, const void* UV,
@@ -152,7 +155,8 @@ fb_status_t attn_fwd(const void* Q, const void* K, const void* V, const void* dO
  * (rowsum(dO * O)). Scratch (a B*H*N float32 vector when D_out is NULL, and for
  * bf16/fp16 inputs the partial sums of a split streamed range, sized like
  * bob_workspace_bytes' split records) is allocated with hipMallocAsync and freed
- * with hipFreeAsync on `stream`; FB_ERR_OOM if that fails. bf16/fp16 inputs run
+ * with hipFreeAsync on `stream`; FB_ERR_OOM (nothing launched) under the same
+ * conditions as bob_attention. bf16/fp16 inputs run
  * the staged kernels of pass 1 and pass 2 restricted to S and dP; float32 inputs
  * run single-buffered kernels.
  */
@@ -169,6 +173,15 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
  * kernel, so results do not depend on scheduling.
  */
 fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits);
+
+/*
+ * fb_set_alloc_limit: process-wide cap, in bytes, on each device allocation the
+ * library makes itself (bob_attention's workspace, attn_bwd's scratch); 0 (the
+ * default) means no cap. A larger request returns FB_ERR_OOM before any HIP
+ * call, which lets a caller hold the library to a memory budget. The _ws entry
+ * points allocate nothing and ignore it. Always returns FB_OK.
+ */
+fb_status_t fb_set_alloc_limit(size_t bytes);
 
 /*
  * Kernel timing: fb_profile_start(only) makes every later launch of the

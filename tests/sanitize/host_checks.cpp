@@ -1,0 +1,115 @@
+// Host-only driver for the C ABI's argument checks, workspace sizing and error
+// reporting, built with AddressSanitizer and UndefinedBehaviorSanitizer on the
+// CPU (tests/test_host_sanitizers.py). The kernel launch functions are replaced
+// by stubs that touch no memory and report an error, so any call that passes its
+// checks ends with FB_ERR_HIP instead of a launch; no GPU is needed.
+#include <climits>
+#include <cstdio>
+#include <cstring>
+
+#include "flashbob.h"
+#include "kernels.hpp"
+
+namespace fb {
+#define FB_STUB(sig) \
+  hipError_t sig { return hipErrorInvalidValue; }
+FB_STUB(launch_attn_fwd(const FwdArgs&, DT, int, bool, int, hipStream_t))
+FB_STUB(launch_attn_fwd_combine(const FwdArgs&, DT, int, hipStream_t))
+FB_STUB(launch_pass1(const Pass1Args&, DT, int, bool, hipStream_t))
+FB_STUB(launch_pass1_d64(const Pass1Args&, DT, bool, hipStream_t))
+FB_STUB(launch_pass1_d128(const Pass1Args&, DT, bool, hipStream_t))
+FB_STUB(launch_pass1_combine(const Pass1Args&, DT, int, hipStream_t))
+FB_STUB(launch_fourpass_sweep(const Pass1Args&, int, DT, int, bool, hipStream_t))
+FB_STUB(launch_first_bwd_dq(const Pass1Args&, DT, int, bool, hipStream_t))
+FB_STUB(launch_first_bwd_dkdv(const Pass2Args&, DT, int, bool, hipStream_t))
+FB_STUB(launch_pass2(const Pass2Args&, DT, int, bool, hipStream_t))
+FB_STUB(launch_pass2_d128(const Pass2Args&, DT, hipStream_t))
+FB_STUB(launch_pass2_reduce(const Pass2Args&, DT, int, hipStream_t))
+FB_STUB(launch_bwd_rowdot(const BwdArgs&, DT, int, int, hipStream_t))
+FB_STUB(launch_bwd_dq(const BwdArgs&, DT, int, bool, int, hipStream_t))
+FB_STUB(launch_bwd_dkdv(const BwdArgs&, DT, int, bool, int, hipStream_t))
+#undef FB_STUB
+}  // namespace fb
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      std::printf("FAIL line %d: %s (%s)\n", __LINE__, #cond, fb_last_error()); \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+static void* fake(int i) { return reinterpret_cast<void*>(0x100000 + 0x1000 * (size_t)i); }
+
+static fb_status_t bob_ws(int B, int H, int N, int d, fb_dtype_t dt, float tau, void* ws, size_t ws_bytes) {
+  return bob_attention_ws(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), tau, 0, B, H, N, d, dt,
+                          fake(7), fake(8), fake(9), fake(10), ws, ws_bytes, nullptr);
+}
+
+int main() {
+  const fb_dtype_t dts[3] = {FB_F32, FB_F16, FB_BF16};
+  const int ns[] = {1, 2, 31, 32, 33, 127, 128, 129, 1000, 16384, 262144, 1 << 22, INT_MAX - 255, INT_MAX - 127,
+                    INT_MAX, -1, 0, INT_MIN};
+  const int bhs[][2] = {{1, 1}, {8, 12}, {65535, 1}, {1, 65535}, {256, 256}, {0, 1}, {-3, 2}};
+  // workspace sizing over extreme shapes: never crashes, 0 exactly when invalid
+  for (fb_dtype_t dt : dts)
+    for (int d : {32, 64, 96, 128})
+      for (auto& bh : bhs)
+        for (int n : ns)
+          for (int s1 : {0, 1, 64}) {
+            EXPECT(fb_set_tuning(s1, s1) == FB_OK);
+            const size_t w = bob_workspace_bytes(bh[0], bh[1], n, d, dt);
+            const long long rows = (long long)bh[0] * bh[1] * n;
+            const bool valid = (d == 64 || d == 128) && bh[0] >= 1 && bh[1] >= 1 && n >= 1 &&
+                               (long long)bh[0] * bh[1] <= 65535 && rows <= INT_MAX - 255;
+            EXPECT((w != 0) == valid);
+            if (valid) EXPECT(w >= (size_t)rows * d * (dt == FB_F32 ? 4 : 2));
+          }
+  EXPECT(fb_set_tuning(0, 0) == FB_OK);
+  EXPECT(fb_set_tuning(-1, 0) == FB_ERR_ARG);
+  EXPECT(fb_set_tuning(0, 65) == FB_ERR_ARG);
+  EXPECT(std::strlen(fb_last_error()) > 0);
+
+  // argument checks of the workspace entry point
+  EXPECT(bob_ws(1, 1, 128, 96, FB_BF16, 0.125f, fake(20), 1u << 30) == FB_ERR_HEADDIM);
+  EXPECT(bob_ws(1, 1, INT_MAX, 64, FB_BF16, 0.125f, fake(20), 1u << 30) == FB_ERR_SHAPE);
+  EXPECT(bob_ws(1, 1, 128, 64, (fb_dtype_t)3, 0.125f, fake(20), 1u << 30) == FB_ERR_DTYPE);
+  EXPECT(bob_ws(1, 1, 128, 64, FB_BF16, 1.f / 0.f, fake(20), 1u << 30) == FB_ERR_ARG);
+  EXPECT(bob_ws(1, 1, 128, 64, FB_BF16, 0.125f, nullptr, 1u << 30) == FB_ERR_WORKSPACE);
+  EXPECT(bob_ws(1, 1, 128, 64, FB_BF16, 0.125f, fake(20), 64) == FB_ERR_WORKSPACE);
+  // valid arguments reach the (stubbed) launch, which reports a HIP error
+  EXPECT(bob_ws(1, 1, 128, 64, FB_BF16, 0.125f, fake(20), 1u << 30) == FB_ERR_HIP);
+  EXPECT(std::strstr(fb_last_error(), "attn_fwd_stats") != nullptr);
+
+  // allocation cap: refused before any HIP call
+  EXPECT(fb_set_alloc_limit(4096) == FB_OK);
+  EXPECT(bob_attention(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), 0.125f, 1, 2, 3, 4096, 128,
+                       FB_F16, fake(7), fake(8), fake(9), fake(10), nullptr) == FB_ERR_OOM);
+  EXPECT(attn_bwd(fake(0), fake(1), fake(2), fake(3), fake(4), (const float*)fake(5), 0.125f, 0, 1, 1, 4096, 64,
+                  FB_BF16, fake(6), fake(7), fake(8), nullptr, nullptr) == FB_ERR_OOM);
+  EXPECT(fb_set_alloc_limit(0) == FB_OK);
+
+  // other entry points' checks
+  EXPECT(attn_fwd(fake(0), fake(1), fake(2), nullptr, 0.125f, 0, 1, 1, 64, 64, FB_BF16, fake(3), (float*)fake(4),
+                  (float*)fake(5), nullptr) == FB_ERR_NULL);
+  EXPECT(attn_fwd(fake(0), fake(1), fake(2), nullptr, 0.125f, 0, 1, 1, 64, 64, FB_BF16, fake(0), (float*)fake(4),
+                  nullptr, nullptr) == FB_ERR_ARG);
+  EXPECT(bob_attention_with_stats(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7),
+                                  (const float*)fake(8), (const float*)((char*)fake(9) + 2), 0.125f, 0, 1, 1, 64, 64,
+                                  FB_BF16, fake(10), fake(11), fake(12), fake(13), nullptr, nullptr, fake(20),
+                                  1u << 30, nullptr) == FB_ERR_ARG);
+  EXPECT(bob_attention_fourpass_ws(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), 0.125f, 0, 1, 1,
+                                   64, 64, FB_F32, fake(7), fake(8), fake(9), fake(10), fake(20), 1u << 30,
+                                   nullptr) == FB_ERR_DTYPE);
+
+  // timing interface with nothing recorded
+  fb_profile_start("bob_pass1");
+  fb_kernel_time_t t[4];
+  EXPECT(fb_profile_stop(t, 4) == 0);
+  fb_profile_start(nullptr);
+  EXPECT(fb_profile_stop(nullptr, 0) == 0);
+
+  std::printf("%s: %d failures\n", failures ? "FAILED" : "ok", failures);
+  return failures ? 1 : 0;
+}

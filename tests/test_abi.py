@@ -81,6 +81,9 @@ def _bob_ws(lib, ptrs=None, tau=0.125, causal=0, B=1, H=1, N=128, d=64, dt=FB_BF
     (dict(B=0), FB_ERR_SHAPE),
     (dict(H=-1), FB_ERR_SHAPE),
     (dict(B=300, H=300), FB_ERR_SHAPE),
+    (dict(N=2147483647), FB_ERR_SHAPE),
+    (dict(N=2147483647 - 127), FB_ERR_SHAPE),
+    (dict(B=2, H=2, N=1 << 29), FB_ERR_SHAPE),
     (dict(dt=7), FB_ERR_DTYPE),
     (dict(tau=float("nan")), FB_ERR_ARG),
     (dict(tau=float("inf")), FB_ERR_ARG),
@@ -133,3 +136,44 @@ def test_other_entry_point_checks(lib):
     st = lib.bob_attention_with_stats(*ptrs, 0.125, 0, 1, 1, 64, 64, FB_BF16, *[v(P + 0x1000 * (10 + i)) for i in range(6)],
                                       v(P), 1 << 40, None)
     assert st == FB_ERR_ARG
+
+
+def test_size_overflow_bounds(lib):
+    """B*H*N beyond 2^31 - 256 is rejected (row tile counts and launch ids are int);
+    sizes just inside the bound give a finite, linear workspace without overflow."""
+    INT_MAX = 2147483647
+    assert lib.bob_workspace_bytes(1, 1, INT_MAX, 64, FB_BF16) == 0
+    assert lib.bob_workspace_bytes(1, 1, INT_MAX - 127, 64, FB_BF16) == 0
+    assert lib.bob_workspace_bytes(65535, 1, 32769, 64, FB_BF16) == 0  # B*H*N just above the bound
+    n_max = INT_MAX - 255
+    w = lib.bob_workspace_bytes(1, 1, n_max, 128, FB_F32)
+    assert w > n_max * 128 * 4  # at least the O buffer, no wrap-around
+    assert w < n_max * 1024 * 4
+    w2 = lib.bob_workspace_bytes(65535, 1, 32767, 64, FB_BF16)
+    assert w2 > 65535 * 32767 * 64 * 2
+    v = ctypes.c_void_p
+    st = lib.attn_fwd(v(P), v(P + 0x1000), v(P + 0x2000), v(0), 0.125, 0, 1, 1, INT_MAX, 64, FB_BF16,
+                      v(P + 0x3000), v(P + 0x4000), None, None)
+    assert st == FB_ERR_SHAPE and b"exceeds" in lib.fb_last_error()
+
+
+def test_alloc_limit_refuses_before_any_hip_call(lib):
+    """With an allocation cap below the need, the allocating entry points return
+    FB_ERR_OOM from the host checks alone (no device here)."""
+    v = ctypes.c_void_p
+    ptrs = [v(P + 0x1000 * i) for i in range(11)]
+    fb.set_alloc_limit(1024)
+    try:
+        st = lib.bob_attention(*ptrs[:7], 0.125, 0, 1, 1, 4096, 64, FB_BF16, *ptrs[7:], None)
+        assert st == FB_ERR_OOM
+        assert b"allocation limit" in lib.fb_last_error()
+        # attn_bwd without D_out needs scratch for D
+        st = lib.attn_bwd(*[v(P + 0x1000 * i) for i in range(6)], 0.125, 0, 1, 1, 4096, 64, FB_BF16,
+                          *[v(P + 0x1000 * (6 + i)) for i in range(4)], None)
+        assert st == FB_ERR_OOM
+        # argument errors still come first
+        bad = list(ptrs)
+        bad[0] = v(0)
+        assert lib.bob_attention(*bad[:7], 0.125, 0, 1, 1, 4096, 64, FB_BF16, *bad[7:], None) == FB_ERR_NULL
+    finally:
+        fb.set_alloc_limit(0)
