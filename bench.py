@@ -31,7 +31,25 @@ METRIC = "BoB ms/call + TFLOP/s (MFMA util) at N=16K,d=64 bf16; max N on 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "useful": 12, "four_pass_exec": 27}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "long16k_kernel_trace.md")
+TRACE_JSON = os.path.join(ROOT, "profiles", "long16k_kernel_trace.json")
 PASS1_SOURCES = ("bob_pass1_vgpr.hip", "pass1_kernel.hpp", "pass1_common.hpp", "common.hpp", "kernels.hpp")
+# library kernel names (fb_profile_start) of one call, in launch order
+KERNELS_PER_CALL = {
+    "two_pass": ("attn_fwd_stats", "attn_fwd_combine", "bob_pass1", "bob_pass1_combine", "bob_pass2",
+                 "bob_pass2_reduce"),
+    "four_pass": ("attn_fwd_stats", "attn_fwd_combine", "fourpass_alpha", "fourpass_energy", "fourpass_rows",
+                  "bob_pass2", "bob_pass2_reduce"),
+}
+# the device kernel (rocprofv3 name prefix) behind each library name at long_16k (bf16, d = 64, non-causal)
+TRACE_KERNELS = {
+    "attn_fwd_stats": "attn_fwd_kernel<fb::BF16, 64, false, true>",
+    "attn_fwd_combine": "attn_fwd_combine_kernel<fb::BF16, 64, true>",
+    "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0>",
+    "bob_pass1_combine": "bob_pass1_combine_kernel<fb::BF16, 64>",
+    "bob_pass2": "bob_pass2_kernel<fb::BF16, 64, false, false>",
+    "bob_pass2_reduce": "bob_pass2_reduce_kernel<fb::BF16, 64>",
+}
 
 
 def flop_unit(w):
@@ -62,6 +80,20 @@ def traffic_from_profile():
     if s.get("source_hash") != pass1_source_hash():
         return None
     return s.get("hbm_bytes_per_launch")
+
+
+def trace_from_profile():
+    """The committed trace digest of the default bench command, if it was taken
+    from the current pass-1 sources: the dominant kernel's average duration over
+    the launches of the roofline timed region."""
+    try:
+        with open(TRACE_JSON) as fh:
+            s = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if s.get("source_hash") != pass1_source_hash():
+        return None
+    return {"avg_ms": s["roofline_region"]["avg_us"] / 1e3}
 
 
 def _csv_rows(directory, suffix):
@@ -119,36 +151,96 @@ def digest_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
     print(json.dumps(summary, indent=1))
 
 
-def digest_trace(trace_dir, out, bench_log=None):
-    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+def digest_trace(trace_dir, out, bench_log):
+    """Summarise a rocprofv3 --kernel-trace run of the default `python3 bench.py`.
+
+    The long_16k calls come first in the run: W warm-up calls, K headline calls (no
+    library events), K calls with HIP events around pass 1 (the roofline region), then
+    K calls per kernel of the breakdown. Launches of each long_16k kernel are taken in
+    launch order, so the headline and roofline regions are launches [W, W + K) and
+    [W + K, W + 2K) of that kernel; the bench line printed by the same traced run
+    (bench_log) gives W, K and its own event timings for comparison."""
+    import statistics
+
     traced = None
-    if bench_log:
-        with open(bench_log) as fh:
-            for line in fh:
-                if line.startswith("{") and '"roofline"' in line:
-                    traced = json.loads(line)
+    with open(bench_log) as fh:
+        for line in fh:
+            if line.startswith("{") and '"roofline"' in line:
+                traced = json.loads(line)
+    if traced is None:
+        raise SystemExit(f"no bench line in {bench_log}")
+    W, K = traced["warmup"], traced["steps"]
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    launches = {}
+    for r in rows:
+        n = r["Kernel_Name"].replace("void fb::", "").split("(")[0]
+        launches.setdefault(n, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+
+    def durations(name, lo, hi):
+        return [(e - s_) / 1e3 for s_, e in launches.get(TRACE_KERNELS[name], [])[lo:hi]]
+
+    def headline_span():
+        first = launches[TRACE_KERNELS["attn_fwd_stats"]][W][0]
+        last = launches[TRACE_KERNELS["bob_pass2_reduce"]][W + K - 1][1]
+        return (last - first) / 1e3 / K
+
+    table = []
+    total = 0.0
+    for name in KERNELS_PER_CALL["two_pass"]:
+        d = durations(name, W, W + K)
+        if not d:
+            continue
+        total += statistics.mean(d)
+        table.append((name, TRACE_KERNELS[name], len(d), statistics.mean(d), min(d), max(d)))
+    dom = durations("bob_pass1", W + K, W + 2 * K)
+    dom_avg = statistics.mean(dom)
+    flops = traced["roofline"]["algorithmic_flops_per_launch"]
+    peak = traced["roofline"]["peak"]
+    frac = flops / (dom_avg * 1e-6) / 1e12 / peak
+    ev_us = traced["roofline"]["avg_launch_ms"] * 1e3
+    span = headline_span()
+    summary = {
+        "workload": "long_16k: B=1,H=1,N=16384,d=64,bf16,non-causal",
+        "source_hash": pass1_source_hash(),
+        "warmup": W, "steps": K,
+        "headline_region": {"kernels": {t[0]: {"launches": t[2], "avg_us": round(t[3], 2), "min_us": round(t[4], 2),
+                                                "max_us": round(t[5], 2)} for t in table},
+                            "sum_of_kernel_avg_us": round(total, 2), "first_to_last_us_per_call": round(span, 2),
+                            "bench_ms_per_step": traced["ms_per_step"]},
+        "roofline_region": {"kernel": "bob_pass1", "launches": len(dom), "avg_us": round(dom_avg, 2),
+                            "min_us": round(min(dom), 2), "max_us": round(max(dom), 2),
+                            "bench_event_avg_us": round(ev_us, 2), "flops_per_launch": flops,
+                            "frac_of_peak": round(frac, 5), "peak_tflops": peak},
+    }
+    cmd = ("rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py "
+           "> <TRACED_STDOUT>")
     lines = ["# Kernel trace: BoB call at long_16k (B=1, H=1, N=16384, d=64, bf16, non-causal)", "",
-             "Commands (repository root, one MI355X):", "", "```",
-             "rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py --steps 5 "
-             "--warmup 2 --no-cpu --no-endpoint --no-parity --no-breakdown > <TRACED_STDOUT>",
+             "Commands (repository root, one MI355X): the default bench run under the kernel tracer, then this "
+             "digest.", "", "```", cmd,
              "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT) + " <TRACED_STDOUT>", "```", "",
              f"Pass-1 source hash ({' + '.join(PASS1_SOURCES)}): {pass1_source_hash()}", "",
-             "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        n = r["Name"].replace("void fb::", "").split("(")[0]
-        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    lines += ["", "Calls: bench.py's 2 warm-up calls, its 5 timed calls (HIP events around pass 1 only), 5 "
-              "repeats without any library events, then the statistics call and 2 + 5 calls of the ledger path "
-              "(pass 1 and pass 2 from saved statistics)."]
-    if traced:
-        r = traced["roofline"]
-        lines += ["", f"The traced bench.py run itself reported {traced['ms_per_step'] * 1e3:.1f} us per call and "
-                  f"{r['avg_launch_ms'] * 1e3:.1f} us per `{r['kernel']}` launch (HIP events, timed region). Under "
-                  "the profiler every kernel runs slower than in an untraced bench.py run, whose figures are the "
-                  "ones reported."]
+             f"## Headline region (launches {W}..{W + K - 1} of each kernel: the {K} timed calls, no library events)",
+             "", "| Library name | Kernel | Launches | Average (us) | Min (us) | Max (us) |", "|---|---|---|---|---|---|"]
+    for name, kern, n, avg, mn, mx in table:
+        lines.append(f"| {name} | `{kern}` | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+    lines += ["", f"Sum of the kernel averages: {total:.1f} us per call; first statistics launch to last "
+              f"reduction end: {span:.1f} us per call; the same traced run's bench line: "
+              f"{traced['ms_per_step'] * 1e3:.1f} us per call (stream events around the {K} calls).", "",
+              f"## Roofline region (launches {W + K}..{W + 2 * K - 1} of pass 1: HIP events around pass 1 only)", "",
+              f"Trace average {dom_avg:.1f} us (min {min(dom):.1f}, max {max(dom):.1f}); the same launches timed by "
+              f"the bench run's HIP events: {ev_us:.1f} us.",
+              f"Pass 1 does 11 units = {flops:.4g} flop per launch, so the trace gives "
+              f"{flops / (dom_avg * 1e-6) / 1e12:.1f} TFLOP/s = {frac:.3f} of the {peak:.0f} TFLOP/s bf16 dense peak "
+              f"(the bench line of that run: {traced['roofline']['frac']:.3f}).", "",
+              "Durations drift by several percent within one run and by up to ~10% between MI355X boxes "
+              "of the pool (clock and power state), so an untraced run on another box reports its own figure; "
+              "this file shows that the trace and the bench's events agree on the same launches.", "",
+              "```json", json.dumps(summary, indent=1), "```"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
+    with open(os.path.splitext(out)[0] + ".json", "w") as fh:
+        json.dump(summary, fh, indent=1)
     print("\n".join(lines))
 
 
@@ -377,37 +469,45 @@ def hutchinson_bench(args, name):
                    "probe": "rademacher"}}), flush=True)
 
 
-def max_n_probe(fb, workload, dev, args):
-    """Largest N (a power of two from 262144 up) whose call runs within the budget.
+def max_n_probe(fb, workload, dev, seed, per_call_s, total_s=None):
+    """Largest N (a power of two from 262144 up; B = H = 1, d = 64, bf16, non-causal)
+    whose call runs within the budget.
 
-    Each size runs once (the library is warmed by a small call first); the
-    next size is tried only if four times this call's time (the N^2 work) fits the
-    budget and the inputs, outputs and workspace fit the free device memory. Each
-    size is checked on two query rows against the oracle (gQ, gdO) and on the key /
-    value shift invariants: sum_j gK_j = 0 and sum_j gV_j = 0 up to rounding, here
-    at most 1e-3 of sum_j |gK_j| (|gV_j|) per head dimension."""
+    Each size runs once (the library is warmed by a small call first). The next
+    size is tried only if four times this call's time (the N^2 work) fits the
+    per-call budget and, with `total_s`, what is left of the total budget, and if
+    its buffers fit the free device memory. Each size is checked on two query rows
+    against the oracle (gQ, gdO) and on the key / value shift invariants: sum_j gK_j
+    = 0 and sum_j gV_j = 0 up to rounding, here at most 1e-3 of sum_j |gK_j| (|gV_j|)
+    per head dimension. Memory per size: torch's peak allocation (inputs, outputs and
+    the library workspace all come from torch) and the drop in the device's free
+    memory (hipMemGetInfo) from before the inputs are allocated to after the call."""
     import numpy as np
     import torch
 
     import oracle
 
     wu = workload.custom(1, 1, 4096, 64, "bf16", False)
-    gu = {k: v.to(dev) for k, v in workload.make_inputs(wu, args.seed).items()}
+    gu = {k: v.to(dev) for k, v in workload.make_inputs(wu, seed).items()}
     fb.bob_attention(*[gu[k] for k in workload.INPUT_NAMES], tau=wu.scale, causal=False)
     torch.cuda.synchronize()
     del gu
+    torch.cuda.empty_cache()
     records = []
     best = None
+    spent = 0.0
     n = 262144
     while True:
         w = workload.custom(1, 1, n, 64, "bf16", False, name=f"probe_{n}")
         need = (fb.workspace_bytes(1, 1, n, 64, w.torch_dtype) + 11 * n * 64 * 2) * 1.1
-        free, _ = torch.cuda.mem_get_info(dev)
-        if need > free:
-            log(f"max-n probe: N={n} needs {need / 2**30:.1f} GiB, {free / 2**30:.1f} GiB free; stop")
+        free0, _ = torch.cuda.mem_get_info(dev)
+        if need > free0:
+            log(f"max-n probe: N={n} needs {need / 2**30:.1f} GiB, {free0 / 2**30:.1f} GiB free; stop")
             break
         log(f"max-n probe: N={n}: generating inputs")
-        cpu_in = workload.make_inputs(w, args.seed)
+        cpu_in = workload.make_inputs(w, seed)
+        torch.cuda.reset_peak_memory_stats(dev)
+        base_alloc = torch.cuda.memory_allocated(dev)
         g = {k: v.to(dev) for k, v in cpu_in.items()}
         log(f"max-n probe: N={n}: call")
         torch.cuda.synchronize()
@@ -415,6 +515,8 @@ def max_n_probe(fb, workload, dev, args):
         out = fb.bob_attention(*[g[k] for k in workload.INPUT_NAMES], tau=w.scale, causal=False)
         torch.cuda.synchronize()
         t = time.perf_counter() - t0
+        spent += t
+        free1, _ = torch.cuda.mem_get_info(dev)
         finite = all(bool(torch.isfinite(o).all()) for o in out)
         shift = {}
         for name, o in (("gK", out[1]), ("gV", out[2])):
@@ -427,9 +529,12 @@ def max_n_probe(fb, workload, dev, args):
         for name, o in (("gQ", out[0]), ("gdO", out[3])):
             got = o[0, 0, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
             errs[name] = float(np.linalg.norm(got - r[name]) / np.linalg.norm(r[name]))
-        ok = finite and max(errs.values()) <= 2e-2 and max(shift.values()) <= 1e-3 and t <= args.max_n_budget
-        rec = {"N": n, "s": round(t, 3), "finite": finite, "row_rel_err": {k: round(v, 6) for k, v in errs.items()},
-               "shift_sum_rel": {k: float(f"{v:.3g}") for k, v in shift.items()}, "ok": ok}
+        ok = finite and max(errs.values()) <= 2e-2 and max(shift.values()) <= 1e-3 and t <= per_call_s
+        rec = {"N": n, "s": round(t, 4), "tflops_21_units": round(UNITS["exec"] * 2.0 * 64 * n * n / t / 1e12, 1),
+               "finite": finite, "row_rel_err": {k: round(v, 6) for k, v in errs.items()},
+               "shift_sum_rel": {k: float(f"{v:.3g}") for k, v in shift.items()},
+               "peak_alloc_bytes": int(torch.cuda.max_memory_allocated(dev) - base_alloc),
+               "hbm_free_drop_bytes": int(free0 - free1), "ok": ok}
         log(f"max-n probe: {rec}")
         records.append(rec)
         del g, out, cpu_in, arrs
@@ -437,11 +542,11 @@ def max_n_probe(fb, workload, dev, args):
         if not ok:
             break
         best = n
-        if 4 * t > args.max_n_budget:
+        if 4 * t > per_call_s or (total_s is not None and 4 * t > total_s - spent):
             break
         n *= 2
-    print(json.dumps({"max_n_run": best, "budget_s": args.max_n_budget, "d": 64, "dtype": "bf16", "probe": records}),
-          flush=True)
+    return {"max_n_run": best, "per_call_budget_s": per_call_s, "total_budget_s": total_s, "d": 64,
+            "dtype": "bf16", "probe": records}
 
 
 def main():
@@ -466,7 +571,9 @@ def main():
                     help="only find the largest N = 2^k >= 262144 (B = H = 1, d = 64, bf16) whose call finishes "
                          "within --max-n-budget seconds and passes sampled oracle rows and the key/value shift "
                          "invariants")
-    ap.add_argument("--max-n-budget", type=float, default=60.0, help="seconds per call for --max-n-probe")
+    ap.add_argument("--max-n-budget", type=float, default=60.0, help="seconds per call for the max-N probe")
+    ap.add_argument("--max-n-total", type=float, default=20.0,
+                    help="seconds of probe calls in the default run (the opt-in --max-n-probe has no total cap)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), to scale HBM counters")
     ap.add_argument("--digest-pmc", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
@@ -475,7 +582,7 @@ def main():
                     help="summarise FETCH_SIZE / WRITE_SIZE runs per workload against the transfer ledger (markdown)")
     ap.add_argument("--digest-sq", nargs="+", metavar="OUT TRACE_DIR DIR=COUNTERS",
                     help="summarise rocprofv3 --pmc runs of matrix-core / issue counters into OUT (markdown)")
-    ap.add_argument("--digest-trace", nargs="+", metavar="TRACE_DIR OUT [BENCH_LOG]",
+    ap.add_argument("--digest-trace", nargs=3, metavar=("TRACE_DIR", "OUT", "BENCH_LOG"),
                     help="summarise a rocprofv3 --kernel-trace --stats run (csv dir) into OUT (markdown)")
     args = ap.parse_args()
     if args.digest_pmc:
@@ -509,7 +616,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     if args.max_n_probe:
-        max_n_probe(fb, workload, dev, args)
+        print(json.dumps(max_n_probe(fb, workload, dev, args.seed, args.max_n_budget)), flush=True)
         return
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -543,42 +650,42 @@ def main():
 
     # dominant kernel: pass 1 (11 units); for the four-pass ablation, its row-output sweep (9 units)
     dom, dom_units = ("bob_pass1", UNITS["pass1"]) if args.schedule == "two_pass" else ("fourpass_rows", 9)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # per-kernel breakdown (untimed): HIP events around every launch of the library
-    kernels = {}
-    if not args.no_breakdown:
-        fb.profile_start()
+    def timed_calls(only=None):
+        """K calls between two stream events; with `only`, the library also records HIP
+        events around every launch of that kernel (on its launch stream)."""
+        torch.cuda.synchronize()
+        if only:
+            fb.profile_start(only)
+        start.record()
         for _ in range(args.steps):
             step()
+        stop.record()
         torch.cuda.synchronize()
-        kernels = fb.profile_stop()
+        rec = fb.profile_stop() if only else {}
+        return start.elapsed_time(stop) / args.steps, rec
 
-    # timed region: whole-call time with stream events; the library records HIP events
-    # around the dominant kernel only, on its launch stream, for the roofline
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    fb.profile_start(dom)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    dom_timed = fb.profile_stop()
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / args.steps
+    # 1. the timed region of the headline: K whole calls, no library events
+    ms, _ = timed_calls()
     log(f"bench: {ms:.4f} ms/call")
-
-    # the same calls without any library events; stream events around each call give
-    # the median and the minimum
+    # 2. the dominant kernel's launch duration for the roofline: K more calls with HIP
+    #    events around that kernel only (the launch-ordered position of these launches is
+    #    what the rocprofv3 trace digest selects)
+    ms_dom_region, dom_timed = timed_calls(dom)
+    # 3. per-kernel breakdown: K calls per kernel, each with events around that kernel alone
+    kernels = {}
+    if not args.no_breakdown:
+        for name in KERNELS_PER_CALL[args.schedule]:
+            _, rec = timed_calls(name)
+            kernels.update(rec)
+    # 4. per-call median and minimum: stream events around each call
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start.record()
     for e0, e1 in evs:
         e0.record()
         step()
         e1.record()
-    stop.record()
     torch.cuda.synchronize()
-    ms_clean = start.elapsed_time(stop) / args.steps
     per_call = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
 
     # the ledger path: pass 1 + pass 2 from saved statistics (19 units), same inputs
@@ -611,11 +718,19 @@ def main():
     p1_flops = dom_units * unit
     p1_tflops = p1_flops / (p1["avg_ms"] * 1e-3) / 1e12
     traffic = traffic_from_profile()
-    if args.schedule != "two_pass":
+    if args.schedule != "two_pass" or w.name != "long_16k":
         traffic = None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(p1_tflops, 3), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(p1_tflops / peak, 5), "traffic": traffic,
-                "algorithmic_flops_per_launch": p1_flops, "avg_launch_ms": p1["avg_ms"]}
+                "algorithmic_flops_per_launch": p1_flops, "avg_launch_ms": p1["avg_ms"],
+                "launches_timed": n_dom}
+    prof = trace_from_profile() if (args.schedule == "two_pass" and w.name == "long_16k") else None
+    if prof:
+        # the committed rocprofv3 trace of this same command (same pass-1 sources):
+        # its average duration of the same launches, and the fraction it gives
+        roofline["profile_avg_launch_ms"] = prof["avg_ms"]
+        roofline["profile_frac"] = round(p1_flops / (prof["avg_ms"] * 1e-3) / 1e12 / peak, 5)
+        roofline["profile"] = os.path.relpath(TRACE_SUMMARY, ROOT)
 
     result = {
         "metric": METRIC,
@@ -635,7 +750,7 @@ def main():
         "roofline": roofline,
         "mfma_util": round(tflops / peak, 5),
         "executed_units": UNITS["exec"] if args.schedule == "two_pass" else UNITS["four_pass_exec"],
-        "ms_per_call_no_kernel_events": round(ms_clean, 5),
+        "ms_per_call_with_pass1_events": round(ms_dom_region, 5),
         "ms_per_call_median": round(per_call[len(per_call) // 2], 5),
         "ms_per_call_min": round(per_call[0], 5),
         "sum_of_kernel_ms_per_call": round(sum(v["avg_ms"] * v["launches"] for v in kern.values()) / args.steps, 5),
@@ -688,28 +803,23 @@ def main():
         result["other_configs"] = others
 
     if not args.no_endpoint:
-        we = workload.WORKLOADS["endpoint_256k"]
-        log(f"bench: feasibility call {we.describe()}")
+        # the 262,144-token feasibility endpoint and, within a bounded total budget,
+        # the doubling probe above it (the longest N whose call runs here)
+        log("bench: feasibility endpoint and bounded max-N probe")
         del g, ws, outs
         torch.cuda.empty_cache()
-        torch.cuda.reset_peak_memory_stats(dev)
-        ge = {k: v.to(dev) for k, v in workload.make_inputs(we, args.seed).items()}
-        out_e = fb.bob_attention(*[ge[n] for n in workload.INPUT_NAMES], tau=we.scale, causal=we.causal)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        out_e = fb.bob_attention(*[ge[n] for n in workload.INPUT_NAMES], tau=we.scale, causal=we.causal)
-        torch.cuda.synchronize()
-        te = time.perf_counter() - t0
-        finite = all(bool(torch.isfinite(o).all()) for o in out_e)
-        free, total = torch.cuda.mem_get_info(dev)
+        probe = max_n_probe(fb, workload, dev, args.seed, args.max_n_budget, args.max_n_total)
+        we = workload.WORKLOADS["endpoint_256k"]
+        _, total = torch.cuda.mem_get_info(dev)
         per_row = (fb.workspace_bytes(1, 1, we.N, we.d, we.torch_dtype) + 11 * we.N * we.d * 2) / we.N
+        end = probe["probe"][0] if probe["probe"] else {}
         result["max_n"] = {
-            "ran_n": we.N, "ran_ms": round(te * 1e3, 2), "finite": finite,
-            "tflops": round(UNITS["exec"] * flop_unit(we) / te / 1e12, 2),
-            "peak_mem_bytes": int(torch.cuda.max_memory_allocated(dev)),
+            "max_n_run": probe["max_n_run"], "total_budget_s": args.max_n_total,
+            "per_call_budget_s": args.max_n_budget,
+            "endpoint_256k": end,
+            "probe": probe["probe"][1:],
             "mem_bound_n_estimate": int(total / per_row),
         }
-        del ge, out_e
 
     if not args.no_cpu:
         log("bench: cpu baseline (fp64 oracle sample)")

@@ -91,7 +91,7 @@ def first_backward_head(q, k, v, do, tau, causal=False):
     return tau * (ds @ k), tau * (ds.T @ q), p.T @ do, dd
 
 
-def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1):
+def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1, row_outputs=True):
     """All BoB quantities for query rows [r0, r1) of one head.
 
     Forward of the first backward (the graph being differentiated), rows R:
@@ -101,7 +101,9 @@ def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1):
     Reverse sweep with cotangents UQ_R on dQ_R, UK on dK, UV on dV, visiting the
     nodes in reverse order. "bar_X" is the cotangent of X.
     Returns the row outputs (gQ_R, gdO_R), the row scalars, and the terms whose
-    transposed products give this block's contribution to gK and gV.
+    transposed products give this block's contribution to gK and gV. With
+    row_outputs=False the four products that only feed gQ_R and gdO_R are not
+    formed (those entries are None); every other value is the same.
     """
     rows = np.arange(r0, r1)
     q_r, do_r, uq_r = q[r0:r1], do[r0:r1], uq[r0:r1]
@@ -115,11 +117,11 @@ def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1):
 
     # node dV = P^T dO  (cotangent UV): feeds bar_P and bar_dO
     bar_p = do_r @ uv.T
-    bar_do = p @ uv
+    bar_do = p @ uv if row_outputs else None
 
     # node dK = tau dS^T Q  (cotangent UK): feeds bar_dS and bar_Q
     bar_ds = tau * (q_r @ uk.T)
-    bar_q = tau * (ds @ uk)
+    bar_q = tau * (ds @ uk) if row_outputs else None
 
     # node dQ = tau dS K  (cotangent UQ_R): feeds bar_dS and bar_K
     bar_ds = bar_ds + tau * (uq_r @ k.T)
@@ -135,14 +137,16 @@ def _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1):
     bar_dp = bar_dp + bar_dd[:, None] * p
 
     # node dP = dO V^T: feeds bar_dO and bar_V (bar_V formed by the caller)
-    bar_do = bar_do + bar_dp @ v
+    if row_outputs:
+        bar_do = bar_do + bar_dp @ v
 
     # node P = softmax(S), row-wise: bar_S = P * (bar_P - rowsum(P * bar_P))
     e_row = np.sum(p * bar_p, axis=1)
     bar_s = p * (bar_p - e_row[:, None])
 
     # node S = tau Q K^T: feeds bar_Q and bar_K (bar_K formed by the caller)
-    bar_q = bar_q + tau * (bar_s @ k)
+    if row_outputs:
+        bar_q = bar_q + tau * (bar_s @ k)
 
     return {
         "gQ": bar_q,
@@ -218,16 +222,21 @@ def bob_rows_head(q, k, v, do, uq, uk, uv, tau, causal, rows):
     return out
 
 
-def bob_cols_head(q, k, v, do, uq, uk, uv, tau, causal, cols, row_block=256):
+def bob_cols_head(q, k, v, do, uq, uk, uv, tau, causal, cols, row_block=256, row_range=None):
     """Column outputs gK[cols], gV[cols] (a full sweep over all query rows, since
-    every row contributes to every column), evaluated on row blocks."""
+    every row contributes to every column), evaluated on row blocks. Each block
+    still forms its rows' scalars D, alpha, E from all keys; the products that
+    only feed the row outputs are skipped. row_range=(r0, r1) restricts the sweep
+    to those query rows: the result is then their exact contribution, and the
+    contributions of disjoint ranges add up to the whole."""
     cols = np.asarray(cols, dtype=np.int64)
     n, d = q.shape
+    lo, hi = (0, n) if row_range is None else (max(0, int(row_range[0])), min(n, int(row_range[1])))
     g_k = np.zeros((len(cols), d))
     g_v = np.zeros((len(cols), d))
-    for r0 in range(0, n, row_block):
-        r1 = min(n, r0 + row_block)
-        t = _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1)
+    for r0 in range(lo, hi, row_block):
+        r1 = min(hi, r0 + row_block)
+        t = _bob_nodes(q, k, v, do, uq, uk, uv, tau, causal, r0, r1, row_outputs=False)
         g_k += tau * (t["_ds"][:, cols].T @ t["_uq"]) + tau * (t["_bar_s"][:, cols].T @ t["_q"])
         g_v += t["_bar_dp"][:, cols].T @ t["_do"]
     return {"gK": g_k, "gV": g_v}

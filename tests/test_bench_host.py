@@ -51,3 +51,43 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_trace_digest_selects_the_timed_launches(tmp_path, monkeypatch):
+    """The trace digest takes each long_16k kernel's launches in launch order: the
+    headline region is [W, W + K) and the roofline region [W + K, W + 2K) of pass 1,
+    whatever else the run launched (other shapes, later regions)."""
+    import csv
+    import json
+
+    W, K = 2, 3
+    names = [bench.TRACE_KERNELS[n] for n in bench.KERNELS_PER_CALL["two_pass"]]
+    rows, t = [], 1000
+    for call in range(W + 3 * K):
+        for i, n in enumerate(names):
+            dur = 1000 * (i + 1) + (100 * call if "pass1_kernel" in n else 0)
+            rows.append({"Kernel_Name": f"void fb::{n}(args)", "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 10
+        # an unrelated kernel of another shape in between
+        rows.append({"Kernel_Name": "void fb::bob_pass1_kernel<fb::BF16, 64, true, 0>(args)",
+                     "Start_Timestamp": t, "End_Timestamp": t + 5})
+        t += 20
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        wr.writeheader()
+        wr.writerows(rows[::-1])  # any order: the digest sorts by start time
+    log = tmp_path / "bench.out"
+    line = {"warmup": W, "steps": K, "ms_per_step": 0.02, "roofline": {
+        "algorithmic_flops_per_launch": 3.0e9, "peak": 2500.0, "avg_launch_ms": 0.0034, "frac": 0.35}}
+    log.write_text("noise\n" + json.dumps(line) + "\n")
+    out = tmp_path / "summary.md"
+    monkeypatch.setattr(bench, "pass1_source_hash", lambda: "abc")
+    bench.digest_trace(str(d), str(out), str(log))
+    summary = json.loads((tmp_path / "summary.json").read_text())
+    p1 = 3000 + 100 * (W + K + 1)  # mean of calls W+K .. W+2K-1
+    assert summary["roofline_region"]["avg_us"] == p1 / 1000
+    assert summary["headline_region"]["kernels"]["bob_pass1"]["avg_us"] == (3000 + 100 * (W + 1)) / 1000
+    assert summary["headline_region"]["kernels"]["attn_fwd_stats"]["launches"] == K
+    assert abs(summary["roofline_region"]["frac_of_peak"] - 3.0e9 / (p1 * 1e-9) / 1e12 / 2500.0) < 1e-4

@@ -330,7 +330,7 @@ def test_workload_gpt2_hessian_sampled_heads():
         assert e <= TOL[w.dtype], (k, e)
 
 
-def _rows_cols_check(w, seed, n_rows, n_cols, col_sum_tol=2e-2):
+def _rows_cols_check(w, seed, n_rows, n_cols, col_sum_tol=2e-2, golden_cols=False):
     fb = _fb()
     _note(f"case {w.describe()} seed={seed}")
     cpu, g = _gpu_inputs(w, seed)
@@ -339,6 +339,8 @@ def _rows_cols_check(w, seed, n_rows, n_cols, col_sum_tol=2e-2):
     del g
     rng = np.random.default_rng(1000 + seed)
     outs = {k: o for k, o in zip(OUTS, out)}
+    if golden_cols:
+        _golden_cols_check(w, cpu, outs)
     for bh in range(w.B * w.H):
         b, h = divmod(bh, w.H)
         arrs = [to_f64(cpu[n][b, h]) for n in workload.INPUT_NAMES]
@@ -363,16 +365,39 @@ def _rows_cols_check(w, seed, n_rows, n_cols, col_sum_tol=2e-2):
             assert ratio <= col_sum_tol, (k, bh, ratio)
 
 
+def _golden_cols_check(w, cpu, outs):
+    """gK, gV on the sampled columns of one head against the stored fp64 oracle values
+    (tests/golden/<workload>_columns.json, written by make_column_goldens.py from the
+    oracle alone); the stored input hashes confirm the same inputs were regenerated."""
+    import hashlib
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"{w.name}_columns.json")
+    gold = json.load(open(path))
+    b, h = gold["head"]
+    assert (gold["N"], gold["d"], gold["dtype"], gold["causal"]) == (w.N, w.d, w.dtype, w.causal)
+    for n in workload.INPUT_NAMES:
+        raw = cpu[n][b, h].contiguous().view(-1).view(torch.uint8).numpy().tobytes()
+        assert hashlib.sha256(raw).hexdigest() == gold["inputs_sha256"][n], f"{n}: regenerated inputs differ"
+    cols = torch.as_tensor(gold["cols"], device=outs["gK"].device)
+    for k in ("gK", "gV"):
+        got = outs[k][b, h, cols].double().cpu().numpy()
+        e = rel(got, np.asarray(gold[k]))
+        _note(f"{w.name} {k} on {len(gold['cols'])} columns: rel error {e:.3e}")
+        assert e <= TOL[w.dtype], (k, e)
+
+
 def test_workload_long_16k():
     _rows_cols_check(workload.WORKLOADS["long_16k"], 0, 96, 48)
 
 
 def test_workload_wide_64k():
-    _rows_cols_check(workload.WORKLOADS["wide_64k"], 0, 32, 0)
+    _rows_cols_check(workload.WORKLOADS["wide_64k"], 0, 32, 0, golden_cols=True)
 
 
 def test_workload_endpoint_256k():
-    _rows_cols_check(workload.WORKLOADS["endpoint_256k"], 0, 32, 0)
+    _rows_cols_check(workload.WORKLOADS["endpoint_256k"], 0, 32, 0, golden_cols=True)
 
 
 # ---- four-pass ablation schedule -----------------------------------------------

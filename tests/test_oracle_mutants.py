@@ -29,6 +29,9 @@ MUTANTS = [
     ("drop tau in S node", "bar_q = bar_q + tau * (bar_s @ k)", "bar_q = bar_q + (bar_s @ k)"),
     ("drop dS^T UQ in gK", "g_k += tau * (t[\"_ds\"].T @ t[\"_uq\"]) + ", "g_k += "),
     ("wrong operand in gV", "g_v += t[\"_bar_dp\"].T @ t[\"_do\"]", "g_v += t[\"_bar_dp\"].T @ t[\"_q\"]"),
+    ("column routine drops dS^T UQ", "g_k += tau * (t[\"_ds\"][:, cols].T @ t[\"_uq\"]) + ", "g_k += "),
+    ("column routine uses Q for dO", "g_v += t[\"_bar_dp\"][:, cols].T @ t[\"_do\"]",
+     "g_v += t[\"_bar_dp\"][:, cols].T @ t[\"_q\"]"),
     ("D without P", "dd = np.sum(p * dp, axis=1)\n    ds = p * (dp - dd[:, None])\n\n    # node dV",
      "dd = np.sum(dp, axis=1) / dp.shape[1]\n    ds = p * (dp - dd[:, None])\n\n    # node dV"),
     ("causal mask off by one", "s[cols[None, :] > row_idx[:, None]] = -np.inf", "s[cols[None, :] >= row_idx[:, None] + 2] = -np.inf"),
