@@ -169,7 +169,7 @@ def digest_trace(trace_dir, out, bench_log):
                 traced = json.loads(line)
     if traced is None:
         raise SystemExit(f"no bench line in {bench_log}")
-    W, K = traced["warmup"], traced["steps"]
+    W, K = traced["warmup"] + traced.get("settle_calls", 0), traced["steps"]
     rows = _csv_rows(trace_dir, "kernel_trace.csv")
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     launches = {}
@@ -220,7 +220,8 @@ def digest_trace(trace_dir, out, bench_log):
              "digest.", "", "```", cmd,
              "python3 bench.py --digest-trace <TRACE> " + os.path.relpath(out, ROOT) + " <TRACED_STDOUT>", "```", "",
              f"Pass-1 source hash ({' + '.join(PASS1_SOURCES)}): {pass1_source_hash()}", "",
-             f"## Headline region (launches {W}..{W + K - 1} of each kernel: the {K} timed calls, no library events)",
+             f"## Headline region (launches {W}..{W + K - 1} of each kernel: the {K} timed calls after "
+             f"{traced['warmup']} warm-up and {traced.get('settle_calls', 0)} settle calls, no library events)",
              "", "| Library name | Kernel | Launches | Average (us) | Min (us) | Max (us) |", "|---|---|---|---|---|---|"]
     for name, kern, n, avg, mn, mx in table:
         lines.append(f"| {name} | `{kern}` | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
@@ -556,6 +557,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_16k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="after the warm-up calls, untimed calls for this long (clock settle)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-endpoint", action="store_true",
@@ -646,7 +649,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("bench: warmup done")
+    # The MI355X takes tens of milliseconds of sustained load to reach a steady clock
+    # (pass 1 measured ~400 -> 460 -> 348 us over its first ~45 calls), so the warm-up
+    # calls are followed by untimed calls until --settle-s seconds have passed.
+    settle_calls = 0
+    t_settle = time.perf_counter() + args.settle_s
+    while time.perf_counter() < t_settle:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle_calls += 10
+    log(f"bench: warmup done (+{settle_calls} settle calls)")
 
     # dominant kernel: pass 1 (11 units); for the four-pass ablation, its row-output sweep (9 units)
     dom, dom_units = ("bob_pass1", UNITS["pass1"]) if args.schedule == "two_pass" else ("fourpass_rows", 9)
@@ -749,6 +762,7 @@ def main():
                    "tau": w.scale, "seed": args.seed, "schedule": args.schedule},
         "roofline": roofline,
         "mfma_util": round(tflops / peak, 5),
+        "settle_calls": settle_calls,
         "executed_units": UNITS["exec"] if args.schedule == "two_pass" else UNITS["four_pass_exec"],
         "ms_per_call_with_pass1_events": round(ms_dom_region, 5),
         "ms_per_call_median": round(per_call[len(per_call) // 2], 5),
