@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     bob_attention,
     bob_attention_alloc,
     bob_attention_fourpass,
+    bob_attention_noalloc,
     bob_attention_with_stats,
     load_library,
     profile_start,

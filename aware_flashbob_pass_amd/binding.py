@@ -30,6 +30,7 @@ SIGNATURES = {
     "fb_last_error": (ctypes.c_char_p, []),
     "bob_attention": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "bob_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "bob_attention_noalloc": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "bob_attention_ws": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P, _S, _P]),
     "bob_attention_fourpass_ws": (_I, [_P] * 7 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P, _S, _P]),
     "bob_attention_with_stats": (_I, [_P] * 10 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 6 + [_P, _S, _P]),
@@ -172,6 +173,19 @@ def bob_attention_alloc(q, k, v, do, uq, uk, uv, tau=None, causal=False):
     _check(load_library().bob_attention(*[_ptr(t) for t in (q, k, v, do, uq, uk, uv)], _tau(tau, d),
                                         int(bool(causal)), B, H, N, d, _DT[ref.dtype], *[_ptr(t) for t in outs],
                                         _stream()))
+    return tuple(outs)
+
+
+def bob_attention_noalloc(q, k, v, do, uq, uk, uv, tau=None, causal=False, out=None):
+    """As bob_attention, through the entry point that allocates nothing on the device
+    (the library's fixed 64 MiB scratch array); only the outputs are allocated here,
+    unless `out` gives them."""
+    ref = _check_inputs([("q", q), ("k", k), ("v", v), ("do", do), ("uq", uq), ("uk", uk), ("uv", uv)])
+    B, H, N, d = ref.shape
+    outs = list(out) if out is not None else [torch.empty_like(ref) for _ in range(4)]
+    _check(load_library().bob_attention_noalloc(*[_ptr(t) for t in (q, k, v, do, uq, uk, uv)], _tau(tau, d),
+                                                int(bool(causal)), B, H, N, d, _DT[ref.dtype],
+                                                *[_ptr(t) for t in outs], _stream()))
     return tuple(outs)
 
 

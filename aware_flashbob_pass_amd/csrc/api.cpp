@@ -92,6 +92,36 @@ fb_status_t device_alloc(void** p, size_t bytes, hipStream_t s, const char* what
   return FB_OK;
 }
 
+// ---- fixed device scratch (bob_attention_noalloc) -------------------------------
+// A file-scope device array serves as the workspace of the entry point that
+// allocates nothing. Each GPU the library runs on holds its own copy from module
+// load until the process ends. In host code `scratch` names only a host-side
+// stand-in, so the device address of each GPU's copy is looked up once per device
+// (with that device current) and every host use goes through that address.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fb_status_t hip_fail(hipError_t e, const char* what);
+
+fb_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FB_ERR_ARG, "device %d out of range [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e == hipSuccess ? hipErrorInvalidSymbol : e, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FB_OK;
+}
+
 // ---- kernel timing ------------------------------------------------------------
 struct ProfRec {
   std::string name;
@@ -404,6 +434,22 @@ fb_status_t bob_attention(const void* Q, const void* K, const void* V, const voi
   }
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
   return ok();
+}
+
+fb_status_t bob_attention_noalloc(const void* Q, const void* K, const void* V, const void* dO, const void* UQ,
+                                  const void* UK, const void* UV, float tau, int causal, int B, int H, int N, int d,
+                                  fb_dtype_t dtype, void* gQ, void* gK, void* gV, void* gdO, hipStream_t stream) {
+  fb_status_t st = check_shape(B, H, N, d, dtype, tau);
+  if (st) return st;
+  const size_t bytes = layout(B, H, N, d, dtype).total;
+  if (bytes > kScratchBytes)
+    return fail(FB_ERR_WORKSPACE, "this shape needs %zu bytes of scratch, more than the %zu-byte maximum of "
+                "bob_attention_noalloc (use bob_attention_ws)", bytes, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return bob_attention_ws(Q, K, V, dO, UQ, UK, UV, tau, causal, B, H, N, d, dtype, gQ, gK, gV, gdO, ws,
+                          kScratchBytes, stream);
 }
 
 fb_status_t bob_attention_with_stats(const void* Q, const void* K, const void* V, const void* dO, const void* UQ,

@@ -103,6 +103,22 @@ fb_status_t bob_attention_ws(const void* Q, const void* K, const void* V, const 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bob_attention_noalloc: as bob_attention, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It calls no hipMalloc, hipFree or allocating routine:
+ * its workspace is a fixed 64 MiB device array inside the library, one copy per
+ * GPU, held from the library's load until the process ends. Shapes whose
+ * workspace (bob_workspace_bytes) exceeds 64 MiB return FB_ERR_WORKSPACE with
+ * nothing launched. Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller. The array's contents on entry are ignored.
+ */
+fb_status_t bob_attention_noalloc(const void* Q, const void* K, const void* V, const void* dO,
+                                  const void* UQ, const void* UK, const void* UV,
+                                  float tau, int causal, int B, int H, int N, int d, fb_dtype_t dtype,
+                                  void* gQ, void* gK, void* gV, void* gdO, hipStream_t stream);
+
+/*
  * bob_attention_fourpass_ws: the same result as bob_attention_ws through the
  * natural four-pass schedule that the method's affine structure collapses to
  * two (review page, Summary; Strengths on Prop. 4.1): after the statistics
