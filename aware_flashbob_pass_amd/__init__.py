@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     profile_start,
     profile_stop,
     set_alloc_limit,
+    set_reduction,
     set_tuning,
     workspace_bytes,
 )

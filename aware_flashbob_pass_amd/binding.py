@@ -38,6 +38,7 @@ SIGNATURES = {
     "attn_bwd": (_I, [_P] * 6 + [_F, _I, _I, _I, _I, _I, _I] + [_P] * 4 + [_P]),
     "fb_set_tuning": (_I, [_I, _I]),
     "fb_set_alloc_limit": (_I, [_S]),
+    "fb_set_reduction": (_I, [_I]),
     "fb_profile_start": (None, [ctypes.c_char_p]),
     "fb_profile_stop": (_I, [ctypes.POINTER(KernelTime), _I]),
 }
@@ -116,6 +117,12 @@ def workspace_bytes(B, H, N, d, dtype):
 
 def set_tuning(pass1_splits=0, pass2_splits=0):
     _check(load_library().fb_set_tuning(int(pass1_splits), int(pass2_splits)))
+
+
+def set_reduction(mode=0):
+    """Pass 2's split reduction: 0 records + merge kernel, 1 float32 atomics, 2 last
+    workgroup merges (see fb_set_reduction in flashbob.h)."""
+    _check(load_library().fb_set_reduction(int(mode)))
 
 
 def set_alloc_limit(nbytes=0):

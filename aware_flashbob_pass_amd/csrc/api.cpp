@@ -42,6 +42,7 @@ fb_status_t ok() {
 // ---- tuning -------------------------------------------------------------------
 std::mutex g_tune_mu;
 int g_split1 = 0, g_split2 = 0;
+int g_reduce = fb::kReduceRecords;  // pass 2's split reduction (fb_set_reduction)
 constexpr int kMaxSplits = 64;
 constexpr int kTargetBlocks = 256;   // one workgroup per compute unit
 constexpr int kMinTilesPerSplit = 4; // 4 x 32 streamed rows per split at least
@@ -202,8 +203,9 @@ DT to_dt(fb_dtype_t t) { return t == FB_BF16 ? DT::BF16 : (t == FB_F16 ? DT::F16
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t o, l, dd, alpha, e, l2, cc, part, total;
+  size_t o, l, dd, alpha, e, l2, cc, part, acc32, counters, total;
   int s0, s1, s2;  // splits of the statistics kernel, pass 1, pass 2
+  int reduce;      // pass 2's split reduction (16-bit inputs with s2 > 1)
 };
 
 WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
@@ -234,6 +236,14 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   const size_t p0 = w.s0 > 1 ? (size_t)w.s0 * tiles * fb::fwd_record_floats(d) * sizeof(float) : 0;
   w.part = off;  // each kernel's records are consumed before the next kernel writes its own
   off += align256(std::max(p0, std::max(p1, p2)));
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    w.reduce = (dtype != FB_F32 && w.s2 > 1) ? g_reduce : fb::kReduceRecords;
+  }
+  w.acc32 = off;
+  if (w.reduce == fb::kReduceAtomic) off += align256((size_t)2 * BH * N * d * sizeof(float));
+  w.counters = off;
+  if (w.reduce == fb::kReduceLastBlock) off += align256((size_t)fb::row_tiles(N) * BH * sizeof(unsigned));
   w.total = off;
   return w;
 }
@@ -257,9 +267,20 @@ fb_status_t column_pass(const void* Q, const void* K, const void* V, const void*
   p2.c = reinterpret_cast<const float*>(ws + w.cc);
   p2.part = reinterpret_cast<float*>(ws + w.part);
   p2.tau = tau; p2.N = N; p2.BH = BH; p2.nsplit = w.s2;
-  fb_status_t st = run("bob_pass2", s, [&] { return fb::launch_pass2(p2, dt, d, causal, s); });
+  p2.reduce = w.reduce;
+  p2.acc32 = reinterpret_cast<float*>(ws + w.acc32);
+  p2.counters = reinterpret_cast<unsigned*>(ws + w.counters);  // zeroed by pass 1
+  fb_status_t st;
+  if (w.reduce == fb::kReduceAtomic) {
+    st = run("bob_pass2_zero", s, [&] { return fb::launch_zero_f32(p2.acc32, (size_t)2 * BH * N * d, s); });
+    if (st) return st;
+  }
+  st = run("bob_pass2", s, [&] { return fb::launch_pass2(p2, dt, d, causal, s); });
   if (st) return st;
-  if (w.s2 > 1) {
+  if (w.reduce == fb::kReduceAtomic) {
+    st = run("bob_pass2_convert", s, [&] { return fb::launch_pass2_convert(p2, dt, d, s); });
+    if (st) return st;
+  } else if (w.s2 > 1 && w.reduce == fb::kReduceRecords) {
     st = run("bob_pass2_reduce", s, [&] { return fb::launch_pass2_reduce(p2, dt, d, s); });
     if (st) return st;
   }
@@ -280,6 +301,7 @@ fb_status_t two_pass(const void* Q, const void* K, const void* V, const void* dO
   p1.c = reinterpret_cast<float*>(ws + w.cc);
   p1.part = reinterpret_cast<float*>(ws + w.part);
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
+  if (w.reduce == fb::kReduceLastBlock) p1.p2_counters = reinterpret_cast<unsigned*>(ws + w.counters);
   fb_status_t st = run("bob_pass1", s, [&] { return fb::launch_pass1(p1, dt, d, causal, s); });
   if (st) return st;
   if (w.s1 > 1) {
@@ -303,6 +325,7 @@ fb_status_t four_pass(const void* Q, const void* K, const void* V, const void* d
   p1.c = reinterpret_cast<float*>(ws + w.cc);
   p1.part = reinterpret_cast<float*>(ws + w.part);
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
+  if (w.reduce == fb::kReduceLastBlock) p1.p2_counters = reinterpret_cast<unsigned*>(ws + w.counters);
   static const char* names[3] = {"fourpass_alpha", "fourpass_energy", "fourpass_rows"};
   for (int sweep = 0; sweep < 3; ++sweep) {
     // The scalar sweeps (and the rows sweep at d = 64) run two workgroups per CU,
@@ -330,6 +353,14 @@ fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   g_split1 = pass1_splits;
   g_split2 = pass2_splits;
+  return ok();
+}
+
+fb_status_t fb_set_reduction(int mode) {
+  if (mode < fb::kReduceRecords || mode > fb::kReduceLastBlock)
+    return fail(FB_ERR_ARG, "reduction mode %d not in {0, 1, 2}", mode);
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_reduce = mode;
   return ok();
 }
 

@@ -18,6 +18,7 @@
 // This file holds the float32 kernel, the split reduce and the launches; the
 // staged 16-bit kernel template is in pass2_kernel.hpp (its non-causal d = 128 BoB
 // instances are built in bob_pass2_vgpr.hip).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -171,6 +172,52 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
     dV += v4;
   }
   pass2_epilogue_quad<TT, D>(dK, dV, kj, g, bh, mb, r4, a);
+}
+
+// kReduceAtomic: clear the float32 sums (a fill kernel, so that the call can be
+// captured in a HIP graph) ...
+__global__ __launch_bounds__(kBlock) void zero_f32_kernel(float* p, size_t n) {
+  for (size_t i = ((size_t)blockIdx.x * kBlock + threadIdx.x) * 4; i < n; i += (size_t)gridDim.x * kBlock * 4) {
+    if (i + 4 <= n) *reinterpret_cast<f32x4*>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+    else
+      for (size_t j = i; j < n; ++j) p[j] = 0.f;
+  }
+}
+
+// ... and convert them afterwards: gK = tau * (sum of dS^T UQ + Sbar^T Q), gV = sum.
+template <class TT, int D>
+__global__ __launch_bounds__(kBlock) void pass2_convert_kernel(Pass2Args a) {
+  using T = typename TT::elem;
+  const size_t plane = (size_t)a.BH * a.N * D;
+  for (size_t i = ((size_t)blockIdx.x * kBlock + threadIdx.x) * 4; i < plane; i += (size_t)gridDim.x * kBlock * 4) {
+    const f32x4 k = *reinterpret_cast<const f32x4*>(a.acc32 + i);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.acc32 + plane + i);
+    store4<TT>(reinterpret_cast<T*>(a.gK) + i, a.tau * k[0], a.tau * k[1], a.tau * k[2], a.tau * k[3]);
+    store4<TT>(reinterpret_cast<T*>(a.gV) + i, v[0], v[1], v[2], v[3]);
+  }
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
+  const size_t blocks = std::min<size_t>(4096, (n / 4 + kBlock - 1) / kBlock + 1);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_pass2_convert(const Pass2Args& a, DT dt, int d, hipStream_t s) {
+  const size_t plane = (size_t)a.BH * a.N * d;
+  const dim3 grid((unsigned)std::min<size_t>(4096, (plane / 4 + kBlock - 1) / kBlock));
+  switch (dt) {
+    case DT::BF16:
+      if (d == 64) hipLaunchKernelGGL((pass2_convert_kernel<BF16, 64>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((pass2_convert_kernel<BF16, 128>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case DT::F16:
+      if (d == 64) hipLaunchKernelGGL((pass2_convert_kernel<F16, 64>), grid, dim3(kBlock), 0, s, a);
+      else hipLaunchKernelGGL((pass2_convert_kernel<F16, 128>), grid, dim3(kBlock), 0, s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <class TT, int D, bool CAUSAL>

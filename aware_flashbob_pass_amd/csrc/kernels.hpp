@@ -34,6 +34,16 @@ struct Pass1Args {
   float* part;    // split records (nsplit > 1)
   float tau;
   int N, BH, nsplit;
+  // Pass 2's merge counters ([B*H][row_tiles(N)]), zeroed by pass 1 for the
+  // last-arriving-workgroup reduction (null otherwise).
+  unsigned* p2_counters = nullptr;
+};
+
+// How pass 2 combines the partial gK, gV of a split query range.
+enum Reduce : int {
+  kReduceRecords = 0,    // per-split records, summed in split order by a merge kernel
+  kReduceAtomic = 1,     // float32 atomic additions into acc32, then a conversion kernel
+  kReduceLastBlock = 2,  // records; the last workgroup of a key tile to finish sums them
 };
 
 // Pass 2 (key-tile parallel): gK, gV; or per-split partials.
@@ -45,6 +55,9 @@ struct Pass2Args {
   float* part;
   float tau;
   int N, BH, nsplit;
+  int reduce = kReduceRecords;  // with nsplit > 1 (16-bit BoB sweeps)
+  float* acc32 = nullptr;       // kReduceAtomic: [2][B*H][N][d] float32 (gK / tau, gV), zeroed first
+  unsigned* counters = nullptr; // kReduceLastBlock: [B*H][row_tiles(N)], zero on entry
 };
 
 // First backward: D = rowsum(dO * O), then dQ (query-parallel) and dK, dV (key-parallel).
@@ -97,6 +110,9 @@ hipError_t launch_pass2(const Pass2Args& a, DT dt, int d, bool causal, hipStream
 // The non-causal d = 128 BoB sweep of pass 2, 16-bit inputs (VGPR form, its own translation unit).
 hipError_t launch_pass2_d128(const Pass2Args& a, DT dt, hipStream_t s);
 hipError_t launch_pass2_reduce(const Pass2Args& a, DT dt, int d, hipStream_t s);
+// kReduceAtomic: zero the float32 sums before pass 2, convert them to gK, gV after it.
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+hipError_t launch_pass2_convert(const Pass2Args& a, DT dt, int d, hipStream_t s);
 hipError_t launch_bwd_rowdot(const BwdArgs& a, DT dt, int d, int BH, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, DT dt, int d, bool causal, int BH, hipStream_t s);

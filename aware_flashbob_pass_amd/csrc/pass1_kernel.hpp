@@ -188,6 +188,8 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   int qt, bh;
   tile_and_head<CAUSAL, true>(qt, bh);
   const int N = a.N, split = blockIdx.z / NH, half = blockIdx.z % NH;
+  // pass 2's merge counter of key tile qt starts at zero (kReduceLastBlock)
+  if (a.p2_counters && blockIdx.z == 0 && threadIdx.x == 0) a.p2_counters[(size_t)bh * row_tiles(N) + qt] = 0u;
   const size_t base = (size_t)bh * N * D;
   const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base,
                       reinterpret_cast<const T*>(a.UK) + base, reinterpret_cast<const T*>(a.UV) + base};

@@ -55,6 +55,66 @@ __device__ inline void pass2_write_record(const f32x16 (&dK)[Geo<TT, D>::MB], co
   }
 }
 
+// kReduceAtomic: add one wave's partial sums into the float32 buffers (gK without its
+// factor tau, gV) with hardware float32 atomics; the order of the additions from
+// different splits is not fixed, so results may differ in the last bits between runs.
+template <class TT, int D>
+__device__ inline void pass2_atomic_add(const f32x16 (&dK)[Geo<TT, D>::MB], const f32x16 (&dV)[Geo<TT, D>::MB],
+                                        int kj, int g, int bh, const Pass2Args& a) {
+  if (kj >= a.N) return;
+  const size_t plane = (size_t)a.BH * a.N * D;
+  float* k32 = a.acc32 + ((size_t)bh * a.N + kj) * D;
+  float* v32 = k32 + plane;
+#pragma unroll
+  for (int mb = 0; mb < Geo<TT, D>::MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dim = mb * 32 + kappa(r, g);
+      unsafeAtomicAdd(k32 + dim, dK[mb][r]);
+      unsafeAtomicAdd(v32 + dim, dV[mb][r]);
+    }
+}
+
+// kReduceLastBlock: after a workgroup has written its records, it counts itself in
+// the key tile's counter; the workgroup that arrives last sums every split's records
+// of the tile in split order (the same order as the merge kernel, so the result is
+// bitwise the same as with kReduceRecords), writes gK, gV and resets the counter.
+// The records of other workgroups may sit in another XCD's L2, so the writers
+// release them at device scope before counting and the last one acquires before
+// reading.
+template <class TT, int D>
+__device__ inline void pass2_last_block_merge(int kt, int bh, int wave, int lane, int kj, int g, const Pass2Args& a) {
+  constexpr int MB = Geo<TT, D>::MB;
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.counters + (size_t)bh * row_tiles(a.N) + kt;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (unsigned)a.nsplit - 1;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  f32x16 dK[MB], dV[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    dK[mb] = zero16();
+    dV[mb] = zero16();
+  }
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* R =
+        a.part + ((((size_t)sp * a.BH + bh) * row_tiles(a.N) + kt) * 4 + wave) * pass2_record_floats(D);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      dK[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
+      dV[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+    }
+  }
+  pass2_epilogue<TT, D>(dK, dV, kj, g, bh, a);
+}
+
 // Staged variant for 16-bit inputs: three LDS stages of row-major Q, dO, UQ
 // tiles plus their four row scalars, copied two steps ahead from inline
 // assembly so that the end of a step waits only for the copies of the next one
@@ -258,7 +318,16 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
     pass2_epilogue<TT, D>(accK, accV, kj, g, bh, a);
     return;
   }
+  if constexpr (!FIRST) {
+    if (a.reduce == kReduceAtomic) {
+      pass2_atomic_add<TT, D>(accK, accV, kj, g, bh, a);
+      return;
+    }
+  }
   pass2_write_record<TT, D>(accK, accV, split, bh, kt, wave, lane, a);
+  if constexpr (!FIRST) {
+    if (a.reduce == kReduceLastBlock) pass2_last_block_merge<TT, D>(kt, bh, wave, lane, kj, g, a);
+  }
 }
 
 template <class TT, int D>

@@ -315,6 +315,53 @@ def digest_ledger(out, copy_fetch, copy_write, *runs):
     print("\n".join(lines))
 
 
+def digest_reduction(out, copy_fetch, copy_write, *runs):
+    """Pass 2's three split reductions at long_16k (bench.py --reduction 0/1/2):
+    call time, per-kernel time and HBM bytes of the pass-2 kernels per mode.
+    runs: MODE=FETCH_DIR,WRITE_DIR,BENCH_JSON ..."""
+    copy_bytes = 512 << 20
+    cf, cw = _per_kernel_mean(copy_fetch), _per_kernel_mean(copy_write)
+    ck = [k for k in cf if "copy" in k.lower()][0]
+    ff, wf = copy_bytes / (cf[ck] * 1024), copy_bytes / (cw[ck] * 1024)
+    label = {"0": "split records + merge kernel (default)", "1": "float32 atomics + zero/convert kernels",
+             "2": "split records, merged by the last workgroup of each key tile"}
+    lines = ["# Pass 2's split reduction, measured: long_16k (B=1, H=1, N=16384, d=64, bf16, non-causal)", "",
+             "Pass 2 runs 4 splits of the query range here (128 key tiles x 4 = 512 workgroups, two per CU). "
+             "Commands (repository root, one MI355X; <M> = 0, 1, 2):", "", "```",
+             "python3 bench.py --reduction <M> --no-cpu --no-endpoint --steps 40 > <BENCH_M>",
+             "rocprofv3 --pmc FETCH_SIZE -d <FETCH_M> -o run --output-format csv -- python3 bench.py --reduction <M> "
+             "--steps 5 --warmup 2 --no-cpu --no-endpoint --no-parity --no-breakdown --settle-s 0",
+             "rocprofv3 --pmc WRITE_SIZE -d <WRITE_M> -o run --output-format csv -- python3 bench.py --reduction <M> "
+             "--steps 5 --warmup 2 --no-cpu --no-endpoint --no-parity --no-breakdown --settle-s 0",
+             "rocprofv3 --pmc FETCH_SIZE -d <COPY_FETCH> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+             "rocprofv3 --pmc WRITE_SIZE -d <COPY_WRITE> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
+             "python3 bench.py --digest-reduction " + os.path.relpath(out, ROOT) +
+             " <COPY_FETCH> <COPY_WRITE> <M>=<FETCH_M>,<WRITE_M>,<BENCH_M> ...", "```", "",
+             f"Counter scale from a plain 512 MiB device copy: FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {wf:.3f}.", "",
+             "| Mode | call (ms) | ledger path (ms) | pass-2 kernels (us each, events around that kernel alone) | "
+             "pass-2 HBM read (MB) | pass-2 HBM written (MB) |", "|---|---|---|---|---|---|"]
+    for r in runs:
+        mode, dirs = r.split("=", 1)
+        fdir, wdir, bj = dirs.split(",")
+        f, wr = _per_kernel_mean(fdir), _per_kernel_mean(wdir)
+        with open(bj) as fh:
+            b = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+        kern = {k: v["avg_ms"] * 1e3 for k, v in b["kernels"].items() if k.startswith("bob_pass2")}
+        rd = sum(v for k, v in f.items() if "pass2" in k or "zero_f32" in k) * 1024 * ff
+        wb = sum(v for k, v in wr.items() if "pass2" in k or "zero_f32" in k) * 1024 * wf
+        ks = ", ".join(f"{k} {v:.1f}" for k, v in kern.items())
+        lines.append(f"| {mode}: {label.get(mode, mode)} | {b['ms_per_step']:.4f} | {b['with_stats']['ms_per_call']:.4f} | "
+                     f"{ks} | {rd / 1e6:.1f} | {wb / 1e6:.1f} |")
+    lines += ["", "Mode 0 is kept. The atomic form adds about 8.4 million float32 atomic additions per call "
+              "(64 per lane per split workgroup) at the L2; the last-workgroup form makes every split workgroup "
+              "release its records at device scope (a write-back of its XCD's L2) and the last one acquire them "
+              "(an invalidation), which costs more than the merge kernel it replaces. Modes 0 and 2 are "
+              "deterministic and bitwise equal; mode 1 depends on the order of the atomic additions."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 SQ_COMMAND = ("rocprofv3 --pmc {counters} -d <{tag}> -o run --output-format csv -- python3 bench.py --steps 5 "
               "--warmup 2 --no-cpu --no-endpoint --no-parity")
 KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
@@ -568,6 +615,9 @@ def main():
                     help="skip the untimed pass with HIP events around every kernel (the kernels field is then empty)")
     ap.add_argument("--hutchinson", action="store_true",
                     help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
+    ap.add_argument("--reduction", type=int, choices=(0, 1, 2), default=0,
+                    help="pass 2's split reduction: 0 records + merge kernel, 1 float32 atomics, "
+                         "2 last-workgroup merge (fb_set_reduction)")
     ap.add_argument("--schedule", choices=("two_pass", "four_pass"), default="two_pass",
                     help="four_pass times the ablation schedule (separate alpha, E and row-output sweeps)")
     ap.add_argument("--max-n-probe", action="store_true",
@@ -583,6 +633,8 @@ def main():
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (csv dirs) into OUT (json)")
     ap.add_argument("--digest-ledger", nargs="+", metavar="OUT COPY_FETCH COPY_WRITE WORKLOAD=FETCH,WRITE",
                     help="summarise FETCH_SIZE / WRITE_SIZE runs per workload against the transfer ledger (markdown)")
+    ap.add_argument("--digest-reduction", nargs="+", metavar="OUT COPY_FETCH COPY_WRITE MODE=FETCH,WRITE,BENCH",
+                    help="summarise pass 2's three split reductions (timing json + FETCH/WRITE runs per mode)")
     ap.add_argument("--digest-sq", nargs="+", metavar="OUT TRACE_DIR DIR=COUNTERS",
                     help="summarise rocprofv3 --pmc runs of matrix-core / issue counters into OUT (markdown)")
     ap.add_argument("--digest-trace", nargs=3, metavar=("TRACE_DIR", "OUT", "BENCH_LOG"),
@@ -599,6 +651,9 @@ def main():
         return
     if args.digest_ledger:
         digest_ledger(*args.digest_ledger)
+        return
+    if args.digest_reduction:
+        digest_reduction(*args.digest_reduction)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -634,6 +689,7 @@ def main():
         hutchinson_bench(args, "gpt2_hessian" if args.workload == "long_16k" else args.workload)
         return
     w = workload.WORKLOADS[args.workload]
+    fb.set_reduction(args.reduction)
     log(f"bench: {w.describe()} steps={args.steps} warmup={args.warmup}")
     cpu_in = workload.make_inputs(w, args.seed)
     g = {k: v.to(dev) for k, v in cpu_in.items()}
@@ -687,9 +743,14 @@ def main():
     #    what the rocprofv3 trace digest selects)
     ms_dom_region, dom_timed = timed_calls(dom)
     # 3. per-kernel breakdown: K calls per kernel, each with events around that kernel alone
+    #    (the kernel names of one call come from one call with events around every kernel)
     kernels = {}
     if not args.no_breakdown:
-        for name in KERNELS_PER_CALL[args.schedule]:
+        fb.profile_start()
+        step()
+        torch.cuda.synchronize()
+        names = list(fb.profile_stop())
+        for name in names:
             _, rec = timed_calls(name)
             kernels.update(rec)
     # 4. per-call median and minimum: stream events around each call
@@ -759,7 +820,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "tau": w.scale, "seed": args.seed, "schedule": args.schedule},
+                   "tau": w.scale, "seed": args.seed, "schedule": args.schedule, "reduction": args.reduction},
         "roofline": roofline,
         "mfma_util": round(tflops / peak, 5),
         "settle_calls": settle_calls,

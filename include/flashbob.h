@@ -191,6 +191,20 @@ fb_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O,
 fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits);
 
 /*
+ * fb_set_reduction: how pass 2 combines the partial gK, gV of a split query range
+ * (bf16/fp16 inputs; see fb_set_tuning for when the range is split). Process-wide;
+ * affects bob_workspace_bytes. Returns FB_ERR_ARG for other values.
+ *   0 (default): each split writes a record and a separate kernel sums the
+ *      records in split order (deterministic);
+ *   1: each split adds its sums into float32 buffers with hardware atomics, then a
+ *      conversion kernel writes gK, gV (order of additions not fixed, so results
+ *      may differ in the last bits between runs);
+ *   2: records as in 0, summed in split order by the last workgroup of each key
+ *      tile to finish (deterministic, bitwise equal to 0, no separate kernel).
+ */
+fb_status_t fb_set_reduction(int mode);
+
+/*
  * fb_set_alloc_limit: process-wide cap, in bytes, on each device allocation the
  * library makes itself (bob_attention's workspace, attn_bwd's scratch); 0 (the
  * default) means no cap. A larger request returns FB_ERR_OOM before any HIP

@@ -25,6 +25,8 @@ FB_STUB(launch_first_bwd_dkdv(const Pass2Args&, DT, int, bool, hipStream_t))
 FB_STUB(launch_pass2(const Pass2Args&, DT, int, bool, hipStream_t))
 FB_STUB(launch_pass2_d128(const Pass2Args&, DT, hipStream_t))
 FB_STUB(launch_pass2_reduce(const Pass2Args&, DT, int, hipStream_t))
+FB_STUB(launch_pass2_convert(const Pass2Args&, DT, int, hipStream_t))
+hipError_t launch_zero_f32(float*, size_t, hipStream_t) { return hipErrorInvalidValue; }
 FB_STUB(launch_bwd_rowdot(const BwdArgs&, DT, int, int, hipStream_t))
 FB_STUB(launch_bwd_dq(const BwdArgs&, DT, int, bool, int, hipStream_t))
 FB_STUB(launch_bwd_dkdv(const BwdArgs&, DT, int, bool, int, hipStream_t))
@@ -70,6 +72,16 @@ int main() {
   EXPECT(fb_set_tuning(-1, 0) == FB_ERR_ARG);
   EXPECT(fb_set_tuning(0, 65) == FB_ERR_ARG);
   EXPECT(std::strlen(fb_last_error()) > 0);
+  EXPECT(fb_set_reduction(3) == FB_ERR_ARG);
+  EXPECT(fb_set_reduction(-1) == FB_ERR_ARG);
+  for (int mode = 0; mode < 3; ++mode) {  // workspace sizing in every reduction mode
+    EXPECT(fb_set_reduction(mode) == FB_OK);
+    EXPECT(fb_set_tuning(0, 4) == FB_OK);
+    EXPECT(bob_workspace_bytes(1, 1, 16384, 64, FB_BF16) > 0);
+    EXPECT(bob_workspace_bytes(1, 1, INT_MAX - 255, 128, FB_F16) > 0);
+  }
+  EXPECT(fb_set_reduction(0) == FB_OK);
+  EXPECT(fb_set_tuning(0, 0) == FB_OK);
 
   // argument checks of the workspace entry point
   EXPECT(bob_ws(1, 1, 128, 96, FB_BF16, 0.125f, fake(20), 1u << 30) == FB_ERR_HEADDIM);

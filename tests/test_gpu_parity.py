@@ -423,3 +423,37 @@ def test_fourpass_matches_oracle(dtype, d, causal, N, splits):
     # pass 2 is shared, and sees the same alpha/E up to rounding: the column outputs agree closely
     for k in (1, 2):
         assert rel(to_f64(out[k].cpu()), to_f64(two[k].cpu())) <= 1e-2
+
+
+# ---- pass 2's split reduction (fb_set_reduction) -------------------------------
+@pytest.mark.parametrize("dtype,d,causal,splits", [("bf16", 64, False, (2, 3)), ("bf16", 64, True, (3, 5)),
+                                                   ("fp16", 64, False, (1, 8)), ("bf16", 128, False, (2, 3)),
+                                                   ("bf16", 128, True, (7, 5)), ("fp16", 128, False, (2, 64))])
+def test_pass2_reduction_modes(dtype, d, causal, splits):
+    """The three ways of combining pass 2's split partial sums agree with the oracle;
+    the last-workgroup merge is bitwise equal to the merge kernel (same order) and
+    stays so over repeated calls (its counters are reset); the float32-atomic form
+    differs from it only by rounding order."""
+    fb = _fb()
+    w = workload.custom(1, 2, 1000, d, dtype, causal)
+    cpu, g = _gpu_inputs(w, 31)
+    _note(f"reduction modes {w.describe()} splits={splits}")
+    res = {}
+    fb.set_tuning(*splits)
+    try:
+        for mode in (0, 2, 1):
+            fb.set_reduction(mode)
+            res[mode] = [_run_bob(fb, g, w) for _ in range(3)]
+            torch.cuda.synchronize()
+    finally:
+        fb.set_reduction(0)
+        fb.set_tuning(0, 0)
+    ref = _oracle_full(cpu, w)
+    for mode in (0, 1, 2):
+        errs = call_errors({k: to_f64(o.cpu()) for k, o in zip(OUTS, res[mode][0])}, ref)
+        assert max(errs.values()) <= TOL[dtype], (mode, errs)
+    for rep in range(3):
+        for x, y in zip(res[2][rep], res[0][0]):
+            assert torch.equal(x, y)
+    for x, y in zip(res[1][0], res[0][0]):
+        assert rel(to_f64(x.cpu()), to_f64(y.cpu())) <= 1e-2
