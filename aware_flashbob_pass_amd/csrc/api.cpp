@@ -47,8 +47,8 @@ constexpr int kMaxSplits = 64;
 constexpr int kTargetBlocks = 256;   // one workgroup per compute unit
 constexpr int kMinTilesPerSplit = 4; // 4 x 32 streamed rows per split at least
 
-int auto_splits(int BH, int N, int target = kTargetBlocks) {
-  const long long blocks = (long long)fb::row_tiles(N) * BH;
+int auto_splits(int BH, int N, int target = kTargetBlocks, int tiles = -1) {
+  const long long blocks = (long long)(tiles < 0 ? fb::row_tiles(N) : tiles) * BH;
   if (blocks >= target) return 1;
   const int steps = (N + 31) / 32;
   int s = (int)((target + blocks - 1) / blocks);
@@ -60,9 +60,13 @@ int auto_splits(int BH, int N, int target = kTargetBlocks) {
 // unit holds: the statistics kernel at least two (512 workgroups); 16-bit pass 2
 // at d = 64 two (it is built for two waves per SIMD); pass 1 and the rest one.
 // With an explicit pass-1 split the statistics kernel follows that value.
+// 16-bit inputs at d = 128 run pass 1 with 16-query waves, 64 queries per workgroup.
+bool pass1_uses_q16(fb::DT dt, int d) { return dt != fb::DT::F32 && d == 128; }
+
 void splits_for(int BH, int N, fb::DT dt, int d, int* s0, int* s1, int* s2) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
-  *s1 = g_split1 > 0 ? g_split1 : auto_splits(BH, N);
+  *s1 = g_split1 > 0 ? g_split1
+                     : auto_splits(BH, N, kTargetBlocks, pass1_uses_q16(dt, d) ? fb::pass1_q16_tiles(N) : -1);
   *s2 = g_split2 > 0 ? g_split2 : auto_splits(BH, N, fb::pass2_blocks_per_cu(dt, d) * kTargetBlocks);
   *s0 = g_split1 > 0 ? g_split1 : auto_splits(BH, N, 2 * kTargetBlocks);
 }
@@ -231,7 +235,10 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   off += vec;
   const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
   const int nh = fb::pass1_halves(to_dt(dtype), d);
-  const size_t p1 = w.s1 > 1 ? (size_t)w.s1 * tiles * nh * fb::pass1_record_floats(d / nh) * sizeof(float) : 0;
+  const size_t p1 = w.s1 <= 1 ? 0
+                    : pass1_uses_q16(to_dt(dtype), d)
+                        ? (size_t)w.s1 * fb::pass1_q16_tiles(N) * BH * 4 * fb::pass1_q16_record_floats() * sizeof(float)
+                        : (size_t)w.s1 * tiles * nh * fb::pass1_record_floats(d / nh) * sizeof(float);
   const size_t p2 = w.s2 > 1 ? (size_t)w.s2 * tiles * fb::pass2_record_floats(d) * sizeof(float) : 0;
   const size_t p0 = w.s0 > 1 ? (size_t)w.s0 * tiles * fb::fwd_record_floats(d) * sizeof(float) : 0;
   w.part = off;  // each kernel's records are consumed before the next kernel writes its own
@@ -302,10 +309,15 @@ fb_status_t two_pass(const void* Q, const void* K, const void* V, const void* dO
   p1.part = reinterpret_cast<float*>(ws + w.part);
   p1.tau = tau; p1.N = N; p1.BH = BH; p1.nsplit = w.s1;
   if (w.reduce == fb::kReduceLastBlock) p1.p2_counters = reinterpret_cast<unsigned*>(ws + w.counters);
-  fb_status_t st = run("bob_pass1", s, [&] { return fb::launch_pass1(p1, dt, d, causal, s); });
+  const bool q16 = pass1_uses_q16(dt, d);
+  fb_status_t st = run("bob_pass1", s, [&] {
+    return q16 ? fb::launch_pass1_q16(p1, dt, causal, s) : fb::launch_pass1(p1, dt, d, causal, s);
+  });
   if (st) return st;
   if (w.s1 > 1) {
-    st = run("bob_pass1_combine", s, [&] { return fb::launch_pass1_combine(p1, dt, d, s); });
+    st = run("bob_pass1_combine", s, [&] {
+      return q16 ? fb::launch_pass1_q16_combine(p1, dt, s) : fb::launch_pass1_combine(p1, dt, d, s);
+    });
     if (st) return st;
   }
   return column_pass(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau, causal, BH, N, d, dt, gK, gV, ws, w, s);

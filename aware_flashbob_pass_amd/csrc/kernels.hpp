@@ -94,6 +94,12 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_d128(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
+// Pass 1 with 16-query waves for 16-bit inputs at d = 128 (64 queries per workgroup,
+// every score tile computed once) and its split merge.
+__host__ __device__ inline int pass1_q16_tiles(int N) { return (N + 63) / 64; }
+__host__ __device__ constexpr size_t pass1_q16_record_floats() { return (size_t)(4 * 8 * 4 + 2) * 64; }
+hipError_t launch_pass1_q16(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
+hipError_t launch_pass1_q16_combine(const Pass1Args& a, DT dt, hipStream_t s);
 // Four-pass ablation schedule, 16-bit inputs: sweep 0 writes alpha, sweep 1 E
 // (alpha known), sweep 2 gQ and gdO (alpha and E known); each with its split merge.
 hipError_t launch_fourpass_sweep(const Pass1Args& a, int sweep, DT dt, int d, bool causal, hipStream_t s);

@@ -19,6 +19,8 @@ FB_STUB(launch_pass1(const Pass1Args&, DT, int, bool, hipStream_t))
 FB_STUB(launch_pass1_d64(const Pass1Args&, DT, bool, hipStream_t))
 FB_STUB(launch_pass1_d128(const Pass1Args&, DT, bool, hipStream_t))
 FB_STUB(launch_pass1_combine(const Pass1Args&, DT, int, hipStream_t))
+FB_STUB(launch_pass1_q16(const Pass1Args&, DT, bool, hipStream_t))
+FB_STUB(launch_pass1_q16_combine(const Pass1Args&, DT, hipStream_t))
 FB_STUB(launch_fourpass_sweep(const Pass1Args&, int, DT, int, bool, hipStream_t))
 FB_STUB(launch_first_bwd_dq(const Pass1Args&, DT, int, bool, hipStream_t))
 FB_STUB(launch_first_bwd_dkdv(const Pass2Args&, DT, int, bool, hipStream_t))
