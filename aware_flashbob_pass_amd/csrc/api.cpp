@@ -234,11 +234,10 @@ WsLayout layout(int B, int H, int N, int d, fb_dtype_t dtype) {
   w.cc = off;
   off += vec;
   const size_t tiles = (size_t)fb::row_tiles(N) * BH * 4;  // waves
-  const int nh = fb::pass1_halves(to_dt(dtype), d);
   const size_t p1 = w.s1 <= 1 ? 0
                     : pass1_uses_q16(to_dt(dtype), d)
                         ? (size_t)w.s1 * fb::pass1_q16_tiles(N) * BH * 4 * fb::pass1_q16_record_floats() * sizeof(float)
-                        : (size_t)w.s1 * tiles * nh * fb::pass1_record_floats(d / nh) * sizeof(float);
+                        : (size_t)w.s1 * tiles * fb::pass1_record_floats(d) * sizeof(float);
   const size_t p2 = w.s2 > 1 ? (size_t)w.s2 * tiles * fb::pass2_record_floats(d) * sizeof(float) : 0;
   const size_t p0 = w.s0 > 1 ? (size_t)w.s0 * tiles * fb::fwd_record_floats(d) * sizeof(float) : 0;
   w.part = off;  // each kernel's records are consumed before the next kernel writes its own

@@ -155,10 +155,10 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_simple_kernel(Pass1Args a) {
   }
 
   if (a.nsplit == 1) {
-    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, 0, a);
+    pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
     return;
   }
-  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, blockIdx.x, wave, lane, 0, a);
+  pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, blockIdx.x, wave, lane, a);
 }
 
 template <class TT, int D, int MODE>
@@ -207,14 +207,14 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
   const int L = threadIdx.x >> 2, r4 = threadIdx.x & 3;
   const int g = L >> 5, n = L & 31;
   const int qt = blockIdx.x >> 2, wave = blockIdx.x & 3;
-  const int bh = blockIdx.y, half = blockIdx.z / MB, mbl = blockIdx.z % MB;
+  const int bh = blockIdx.y, mbl = blockIdx.z;
   const int qi = qt * kBlockRows + wave * kTile + n;
   f32x4 acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   float alo = 0.f, ahi = 0.f, elo = 0.f, ehi = 0.f;
   for (int sp = 0; sp < a.nsplit; ++sp) {
-    const float* R = pass1_record<TT, D>(a, sp, bh, qt, wave, half);
+    const float* R = pass1_record<TT, D>(a, sp, bh, qt, wave);
     f32x4 v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(R + ((k * MB + mbl) * 64 + L) * 16 + r4 * 4);
@@ -226,14 +226,14 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
     for (int k = 0; k < 4; ++k) acc[k] += v[k];
   }
   const float alpha = alo + ahi, e0 = elo + ehi;
-  pass1_epilogue_quad<TT, D>(acc[0], acc[1], acc[2], acc[3], alpha, e0, qi, g, bh, half * MB + mbl, r4, a);
+  pass1_epilogue_quad<TT, D>(acc[0], acc[1], acc[2], acc[3], alpha, e0, qi, g, bh, mbl, r4, a);
   if (blockIdx.z == 0 && r4 == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
 }
 
 template <class TT, int D, bool CAUSAL>
 static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
   const size_t lds = pass1_lds_bytes<TT, D>();
-  dim3 grid(row_tiles(a.N), a.BH, a.nsplit * P1<TT, D>::NH);
+  dim3 grid(row_tiles(a.N), a.BH, a.nsplit);
   if constexpr (TT::KPL == 1) {
     hipError_t e = ensure_lds(&bob_pass1_simple_kernel<TT, D, CAUSAL>, lds);
     if (e != hipSuccess) return e;
@@ -241,7 +241,7 @@ static hipError_t launch_p1_t(const Pass1Args& a, hipStream_t s) {
   } else if constexpr (D == 64) {
     return launch_pass1_d64(a, std::is_same_v<TT, BF16> ? DT::BF16 : DT::F16, CAUSAL, s);
   } else if constexpr (D == 128) {
-    return launch_pass1_d128(a, std::is_same_v<TT, BF16> ? DT::BF16 : DT::F16, CAUSAL, s);
+    return hipErrorInvalidValue;  // 16-bit d = 128 runs bob_pass1_q16_kernel (launch_pass1_q16)
   } else {
     hipError_t e = ensure_lds(&bob_pass1_kernel<TT, D, CAUSAL, kTwoPass>, lds);
     if (e != hipSuccess) return e;
@@ -266,7 +266,7 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 
 template <class TT, int D>
 static hipError_t launch_c1_t(const Pass1Args& a, hipStream_t s) {
-  dim3 grid(row_tiles(a.N) * 4, a.BH, P1<TT, D>::NH * P1<TT, D>::MBA);  // one workgroup per wave record
+  dim3 grid(row_tiles(a.N) * 4, a.BH, P1<TT, D>::MBA);  // one workgroup per wave record
   hipLaunchKernelGGL((bob_pass1_combine_kernel<TT, D>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

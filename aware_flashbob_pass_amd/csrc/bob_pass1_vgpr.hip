@@ -1,4 +1,4 @@
-// The two-pass sweeps of pass 1 for 16-bit inputs (d = 64 and 128), in a translation
+// The two-pass sweeps of pass 1 for 16-bit inputs at d = 64, in a translation
 // unit of their own compiled with -mllvm -amdgpu-mfma-vgpr-form: their score products
 // write VGPRs that the element-wise work reads directly, while the four accumulator
 // tiles stay in AGPRs through inline-assembly products (mfma_acc). With the default
@@ -22,24 +22,6 @@ hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t 
   switch (dt) {
     case DT::BF16: return causal ? launch_64<BF16, true>(a, s) : launch_64<BF16, false>(a, s);
     case DT::F16: return causal ? launch_64<F16, true>(a, s) : launch_64<F16, false>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <class TT, bool CAUSAL>
-static hipError_t launch_128(const Pass1Args& a, hipStream_t s) {
-  const size_t lds = pass1_lds_bytes<TT, 128>();
-  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 128, CAUSAL, kTwoPass>, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bob_pass1_kernel<TT, 128, CAUSAL, kTwoPass>),
-                     dim3(row_tiles(a.N), a.BH, a.nsplit * P1<TT, 128>::NH), dim3(kBlock), lds, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_pass1_d128(const Pass1Args& a, DT dt, bool causal, hipStream_t s) {
-  switch (dt) {
-    case DT::BF16: return causal ? launch_128<BF16, true>(a, s) : launch_128<BF16, false>(a, s);
-    case DT::F16: return causal ? launch_128<F16, true>(a, s) : launch_128<F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

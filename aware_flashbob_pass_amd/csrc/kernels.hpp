@@ -72,8 +72,6 @@ struct BwdArgs {
 
 // Float count of one wave's partial record.
 __host__ __device__ inline size_t pass1_record_floats(int d) { return (size_t)(4 * (d / 32) * 16 + 2) * 64; }
-// 16-bit pass 1 at d = 128 splits the accumulated head dimension in halves.
-inline int pass1_halves(DT dt, int d) { return (dt != DT::F32 && d == 128) ? 2 : 1; }
 __host__ __device__ inline size_t fwd_record_floats(int d) { return (size_t)((d / 32) * 16 + 2) * 64; }
 __host__ __device__ inline size_t pass2_record_floats(int d) { return (size_t)(2 * (d / 32) * 16) * 64; }
 __host__ __device__ inline int row_tiles(int N) { return (N + kBlockRows - 1) / kBlockRows; }
@@ -92,7 +90,6 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 // The two-pass sweeps of 16-bit inputs, d = 64 and d = 128 (VGPR form, their own
 // translation unit; called by launch_pass1).
 hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
-hipError_t launch_pass1_d128(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
 // Pass 1 with 16-query waves for 16-bit inputs at d = 128 (64 queries per workgroup,
 // every score tile computed once) and its split merge.

@@ -22,10 +22,7 @@ template <class TT, int D>
 struct P1 {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
-  // 16-bit d = 128: each workgroup accumulates one half of the head dimension
-  // (the grid's z axis holds split x half); everything else accumulates all of it.
-  static constexpr int NH = (TT::KPL == 8 && D == 128) ? 2 : 1;
-  static constexpr int MBA = G::MB / NH;  // accumulated 32-wide head-dim blocks
+  static constexpr int MBA = G::MB;  // accumulated 32-wide head-dim blocks
   // record layout (floats): acc[4][MBA][64 lanes][16], alpha_p[64], e0_p[64]
   static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
 };
@@ -82,37 +79,34 @@ __device__ inline void pass1_write_scalars(float alpha, float e0, int qi, int g,
   a.c[row] = fmaf(alpha, dq, E);
 }
 
-// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave (head-dim
-// blocks half * MBA .. half * MBA + MBA - 1).
+// gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave.
 template <class TT, int D>
 __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
                                       const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
-                                      float alpha_p, float e0_p, int qi, int g, int bh, int half,
-                                      const Pass1Args& a) {
+                                      float alpha_p, float e0_p, int qi, int g, int bh, const Pass1Args& a) {
   constexpr int MBA = P1<TT, D>::MBA;
   const float alpha = pair_sum32(alpha_p);
   const float e0 = pair_sum32(e0_p);
 #pragma unroll
   for (int mbl = 0; mbl < MBA; ++mbl)
-    pass1_epilogue_block<TT, D>(A[mbl], B[mbl], C[mbl], X[mbl], alpha, e0, qi, g, bh, half * MBA + mbl, a);
-  if (half == 0) pass1_write_scalars(alpha, e0, qi, g, bh, a);
+    pass1_epilogue_block<TT, D>(A[mbl], B[mbl], C[mbl], X[mbl], alpha, e0, qi, g, bh, mbl, a);
+  pass1_write_scalars(alpha, e0, qi, g, bh, a);
 }
 
-// Raw accumulators and row partials of one wave for split `split`, half `half`.
+// Raw accumulators and row partials of one wave for split `split`.
 template <class TT, int D>
-__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int qt, int wave, int half) {
-  constexpr int NH = P1<TT, D>::NH;
-  const size_t rec = ((((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave) * NH + half;
-  return a.part + rec * pass1_record_floats(D / NH);
+__device__ inline float* pass1_record(const Pass1Args& a, int split, int bh, int qt, int wave) {
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + qt) * 4 + wave;
+  return a.part + rec * pass1_record_floats(D);
 }
 
 template <class TT, int D>
 __device__ inline void pass1_write_record(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
                                           const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
                                           float alpha_p, float e0_p, int split, int bh, int qt, int wave, int lane,
-                                          int half, const Pass1Args& a) {
+                                          const Pass1Args& a) {
   constexpr int MB = P1<TT, D>::MBA;
-  float* R = pass1_record<TT, D>(a, split, bh, qt, wave, half);
+  float* R = pass1_record<TT, D>(a, split, bh, qt, wave);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);

@@ -139,10 +139,10 @@ __device__ inline void pass1_schedule() {
 // the collapse saves: kAlphaPass sweeps the keys for alpha only (S and G),
 // kEnergyPass sweeps again for E with alpha known, and kRowsPass forms
 // gQ = tau (dS UK + Sbar K) and gdO = P UV + dPbar V with alpha and E known.
-// Waves per SIMD each pass-1 kernel is built for: the two-pass kernel keeps four
-// float32 accumulator tiles in AGPRs beside its score tiles in VGPRs (one wave); the
-// other modes hold at most two accumulator tiles, or at
-// d = 128 at most the alpha sweep's score tiles, and take the register form at two.
+// Waves per SIMD each pass-1 kernel is built for: the two-pass kernel (d = 64; d = 128
+// runs bob_pass1_q16_kernel) keeps four float32 accumulator tiles in AGPRs beside its
+// score tiles in VGPRs (one wave); the other modes hold at most two accumulator tiles,
+// or at d = 128 at most the alpha sweep's score tiles, and take the register form at two.
 __host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
   return (mode == kTwoPass || (d == 128 && mode != kAlphaPass)) ? 1 : 2;
 }
@@ -177,7 +177,6 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   constexpr bool NEED_H = NEED_DP && NEED_G;
   // direct copies one wave issues per step (K always, V for dP, UK for G, UV for H)
   constexpr int COPIES = (1 + NEED_DP + NEED_G + NEED_H) * stage_copies<D, kBlock / 64>();
-  constexpr int NH = TWO ? P1<TT, D>::NH : 1;
   constexpr int MBA = TWO ? P1<TT, D>::MBA : MB;
   static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -187,7 +186,7 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   const int g = lane >> 5, n = lane & 31;
   int qt, bh;
   tile_and_head<CAUSAL, true>(qt, bh);
-  const int N = a.N, split = blockIdx.z / NH, half = blockIdx.z % NH;
+  const int N = a.N, split = blockIdx.z;
   // pass 2's merge counter of key tile qt starts at zero (kReduceLastBlock)
   if (a.p2_counters && blockIdx.z == 0 && threadIdx.x == 0) a.p2_counters[(size_t)bh * row_tiles(N) + qt] = 0u;
   const size_t base = (size_t)bh * N * D;
@@ -385,7 +384,7 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
       // phases 2-3: alpha-free accumulators; rows 8..15 ride along the first half
       V to[2][4];
       auto fetch_tr = [&](int q, V (&o)[4]) {
-        const int t = q / MBA, mb = half * MBA + q % MBA;
+        const int t = q / MBA, mb = q % MBA;
         o[0] = lds_tr_op<TT, D>(ck, mb, t, lane);
         o[1] = lds_tr_op<TT, D>(cuk, mb, t, lane);
         o[2] = lds_tr_op<TT, D>(cv, mb, t, lane);
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
       if constexpr (PIPE) fetch_tr(0, to[0]);
 #pragma unroll
       for (int q = 0; q < NK * MBA; ++q) {
-        const int t = q / MBA, mb = q % MBA;  // mb: accumulator block of this half
+        const int t = q / MBA, mb = q % MBA;
         // d = 128 fetches each k-step's operands just before use (register budget)
         if constexpr (PIPE) {
           if (q + 1 < NK * MBA) fetch_tr(q + 1, to[(q + 1) & 1]);
@@ -476,10 +475,10 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   if constexpr (TWO) {
     if constexpr (ASM_ACC) pass1_acc_settle<MBA>(accA, accB, accC, accX);
     if (a.nsplit == 1) {
-      pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, half, a);
+      pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
       return;
     }
-    pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, half, a);
+    pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, a);
   } else {
     const float sp = MODE == kAlphaPass ? alpha_p : e0_p;
     if (a.nsplit == 1) {

@@ -17,7 +17,6 @@ FB_STUB(launch_attn_fwd(const FwdArgs&, DT, int, bool, int, hipStream_t))
 FB_STUB(launch_attn_fwd_combine(const FwdArgs&, DT, int, hipStream_t))
 FB_STUB(launch_pass1(const Pass1Args&, DT, int, bool, hipStream_t))
 FB_STUB(launch_pass1_d64(const Pass1Args&, DT, bool, hipStream_t))
-FB_STUB(launch_pass1_d128(const Pass1Args&, DT, bool, hipStream_t))
 FB_STUB(launch_pass1_combine(const Pass1Args&, DT, int, hipStream_t))
 FB_STUB(launch_pass1_q16(const Pass1Args&, DT, bool, hipStream_t))
 FB_STUB(launch_pass1_q16_combine(const Pass1Args&, DT, hipStream_t))
