@@ -138,9 +138,9 @@ def digest_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
         "kernels": kernels,
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE -d <FETCH> -o run --output-format csv -- python3 bench.py --steps 5 --warmup 2 "
-            "--no-cpu --no-endpoint --no-parity",
+            "--no-cpu --no-endpoint --no-parity --settle-s 0",
             "rocprofv3 --pmc WRITE_SIZE -d <WRITE> -o run --output-format csv -- python3 bench.py --steps 5 --warmup 2 "
-            "--no-cpu --no-endpoint --no-parity",
+            "--no-cpu --no-endpoint --no-parity --settle-s 0",
             "rocprofv3 --pmc FETCH_SIZE -d <COPY_FETCH> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
             "rocprofv3 --pmc WRITE_SIZE -d <COPY_WRITE> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
             "python3 bench.py --digest-pmc <FETCH> <WRITE> <COPY_FETCH> <COPY_WRITE> " + os.path.relpath(out, ROOT),
@@ -269,9 +269,9 @@ def digest_ledger(out, copy_fetch, copy_write, *runs):
     lines = ["# HBM bytes against the transfer ledger (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
              "Commands (repository root, one MI355X; one counter per run; <W> is the workload):", "", "```",
              "rocprofv3 --pmc FETCH_SIZE -d <FETCH_W> -o run --output-format csv -- python3 bench.py --workload <W> "
-             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown",
+             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown --settle-s 0",
              "rocprofv3 --pmc WRITE_SIZE -d <WRITE_W> -o run --output-format csv -- python3 bench.py --workload <W> "
-             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown",
+             "--steps 1 --warmup 1 --no-cpu --no-endpoint --no-parity --no-breakdown --settle-s 0",
              "rocprofv3 --pmc FETCH_SIZE -d <COPY_FETCH> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
              "rocprofv3 --pmc WRITE_SIZE -d <COPY_WRITE> -o run --output-format csv -- python3 bench.py --calibrate-copy 512",
              "python3 bench.py --digest-ledger " + os.path.relpath(out, ROOT) +
@@ -363,7 +363,7 @@ def digest_reduction(out, copy_fetch, copy_write, *runs):
 
 
 SQ_COMMAND = ("rocprofv3 --pmc {counters} -d <{tag}> -o run --output-format csv -- python3 bench.py --steps 5 "
-              "--warmup 2 --no-cpu --no-endpoint --no-parity")
+              "--warmup 2 --no-cpu --no-endpoint --no-parity --settle-s 0")
 KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
 
 
