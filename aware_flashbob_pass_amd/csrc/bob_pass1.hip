@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void fourpass_combine_kernel(Pass1Args a) {
 
 // Sum the split records of one wave in split order and apply the epilogue. A
 // workgroup takes one wave's record and one 32-wide head-dim block (grid x = query
-// tile x wave, z = half x block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of
+// tile x wave, z = block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of
 // record lane t / 4, so consecutive threads read consecutive 16 bytes and four times
 // as many waves are in flight as with one thread per record lane. The sums are
 // formed in the same order as in one-lane-per-thread form (split by split, then

@@ -7,8 +7,8 @@
 //   gQ = tau (A - alpha B - e0 C),  gdO = X - alpha O,  E = e0 - alpha D.
 //
 // At d = 128 the four float32 accumulators of a 32-query wave would fill the whole
-// register file, so the 32-query kernel splits the accumulated head dimension over
-// two workgroups and computes every score tile twice (16 executed units per pass
+// register file; a 32-query kernel would have to split the accumulated head dimension
+// over two workgroups and compute every score tile twice (16 executed units per pass
 // instead of 11). Here a wave owns 16 queries: its four accumulators take 128
 // registers, each score tile is computed once, and a workgroup of 4 waves (one per
 // SIMD) holds 64 queries.
