@@ -155,21 +155,15 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
   // d = 64: four LDS stages, copies issued three steps ahead from inline assembly
   // and awaited one step before use; d = 128 (no register room for the deeper
-  // unroll) and the unpipelined non-causal d = 64 two-pass sweep (measured 0.7%
-  // faster per call this way) keep three stages, two steps ahead, compiler-visible
-  // copies.
-  constexpr bool DEEP = D == 64 && !(MODE == kTwoPass && !CAUSAL);
+  // unroll) keeps three stages, two steps ahead, compiler-visible copies.
+  constexpr bool DEEP = D == 64;
   constexpr int NT = 4, NBUF = DEEP ? 4 : 3, AHEAD = NBUF - 1;
   // The two-pass sweeps keep their four accumulator tiles in AGPRs from inline
   // assembly and are compiled with the VGPR form for everything else
   // (bob_pass1_vgpr.hip), so the element-wise work reads the score tiles where the
-  // matrix cores wrote them. The causal d = 64 sweep also forms the next step's score
-  // tiles during the current step (software pipelining: 246 VGPRs). The non-causal
-  // d = 64 build of that pipelined form needs more than 256 VGPRs and spills ~50 values
-  // per step, so it forms each step's tiles at the start of the step like d = 128,
-  // which has no room for them either (measured faster than the pipelined sweep in the
-  // default form, whose 64 score-tile copies per step it avoids).
-  constexpr bool PIPE = D == 64 && MODE == kTwoPass && CAUSAL;
+  // matrix cores wrote them. The d = 64 sweeps also form the next step's score tiles
+  // during the current step (software pipelining; 247 VGPRs causal, 255 non-causal).
+  constexpr bool PIPE = D == 64 && MODE == kTwoPass;
   constexpr bool ASM_ACC = MODE == kTwoPass;
   constexpr bool TWO = MODE == kTwoPass;
   constexpr bool NEED_DP = MODE != kAlphaPass;  // the alpha sweep needs S and G only
@@ -347,6 +341,11 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
           const float vwb = p * fmaf(gv, t1, hc[r]);
           alpha_p += vpg;
           e0_p += vwb;
+          // The sums are ordered, so the compiler may not reassociate them; left free it
+          // schedules each chain late and keeps all 32 of the step's terms live (about 50
+          // values spilled per step in the non-causal sweep). Pinning each addition here
+          // keeps a term's live range short. The causal sweep measured 2% slower pinned.
+          if constexpr (!CAUSAL) asm volatile("" : "+v"(alpha_p), "+v"(e0_p));
           vset<TT>(wa[kk], ss, p * t1);
           vset<TT>(wb[kk], ss, vwb);
           vset<TT>(pp[kk], ss, p);
@@ -436,7 +435,8 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
         }
       }
       }
-      if constexpr (PIPE && TWO) pass1_schedule<DK, MBA>();
+      // the interleave request pays off in the causal sweep only (non-causal: 1% slower with it)
+      if constexpr (PIPE && TWO && CAUSAL) pass1_schedule<DK, MBA>();
     } else if (PIPE && act_next) {
 #pragma unroll
       for (int t = 0; t < DK; ++t) {
