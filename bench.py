@@ -151,6 +151,189 @@ def digest_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
     print(json.dumps(summary, indent=1))
 
 
+def _auto_splits(bh, n, target, tiles):
+    """The library's default split count (api.cpp auto_splits), for the dispatch model."""
+    blocks = tiles * bh
+    if blocks >= target:
+        return 1
+    steps = (n + 31) // 32
+    s = (target + blocks - 1) // blocks
+    s = min(s, max(1, steps // 4))
+    return max(1, min(s, 64))
+
+
+def _dispatch_steps(kind, bh, n, causal, tiles, splits):
+    """32-row steps of every workgroup of a launch, in dispatch order, with the
+    fraction of its wave-steps whose wave is active (causal diagonal tiles idle
+    some of the four waves). kind: 'rows' (statistics, pass 1: query tiles, keys
+    streamed) or 'cols' (pass 2: key tiles, queries streamed)."""
+    nst = (n + 31) // 32
+    per_tile = 4 if tiles == (n + 127) // 128 else 2  # 32-row blocks per tile (128- or 64-row tiles)
+    out = []
+    for z in range(splits):
+        for y in range(bh):
+            for x in range(tiles):
+                lin = x + tiles * y
+                rank, head = lin // bh, lin % bh
+                if causal:
+                    tile = (tiles - 1 - rank) if kind == "rows" else rank
+                else:
+                    tile, head = x, y
+                if kind == "rows":
+                    span = min(nst, (tile + 1) * per_tile) if causal else nst
+                    lo, hi = z * span // splits, (z + 1) * span // splits
+                    first = 0
+                else:
+                    first = tile * per_tile if causal else 0
+                    span = nst - first
+                    lo, hi = first + z * span // splits, first + (z + 1) * span // splits
+                steps = hi - lo
+                if causal and steps > 0:
+                    active = 0
+                    for j in range(lo, hi):
+                        if kind == "rows":
+                            active += sum(1 for w in range(per_tile) if j <= tile * per_tile + w)
+                        else:
+                            active += sum(1 for w in range(per_tile) if j >= tile * per_tile + w)
+                    frac = active / (steps * per_tile)
+                else:
+                    frac = 1.0
+                out.append((steps, frac))
+    return out
+
+
+def _makespan(jobs, slots):
+    import heapq
+
+    h = [0.0] * slots
+    for j in jobs:
+        t = heapq.heappop(h)
+        heapq.heappush(h, t + j)
+    return max(h)
+
+
+# kernel families of a BoB call (16-bit): name prefix, how its grid walks the sequence,
+# and workgroups one compute unit holds (d = 64; d = 128 holds one of each)
+SHAPE_KERNELS = (("statistics", "attn_fwd_kernel<", "rows", 2),
+                 ("pass 1", "bob_pass1_kernel<", "rows", 1),
+                 ("pass 1", "bob_pass1_q16_kernel<", "rows", 1),
+                 ("pass 2", "bob_pass2_kernel<", "cols", 2))
+
+
+def _shape_kernel_name(prefix, d, causal, names):
+    c = "true" if causal else "false"
+    for nm in names:
+        if not nm.startswith(prefix):
+            continue
+        args = [a.strip() for a in nm[len(prefix):].rstrip(">").split(",")]
+        if prefix.startswith("bob_pass1_q16"):
+            if d == 128 and args[1] == c:
+                return nm
+        elif args[1] == str(d) and args[2] == c:
+            return nm
+    return None
+
+
+def digest_shapes(trace_dir, bench_log, out):
+    """Summarise the other shapes of a traced default bench run (its other_configs):
+    per-kernel durations of each shape's timed calls (the last launches of kernels that
+    only that shape uses), and for each kernel a dispatch model: the workgroups'
+    32-row step counts in dispatch order, placed greedily on the compute units' slots,
+    priced at the per-step time the same run measured on the 16,384-token head."""
+    import statistics
+
+    traced = None
+    with open(bench_log) as fh:
+        for line in fh:
+            if line.startswith("{") and '"roofline"' in line:
+                traced = json.loads(line)
+    if traced is None or "other_configs" not in traced:
+        raise SystemExit(f"no bench line with other_configs in {bench_log}")
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    launches = {}
+    for r in rows:
+        n = r["Kernel_Name"].replace("void fb::", "").split("(")[0]
+        launches.setdefault(n, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    names = list(launches)
+    W, K = traced["warmup"] + traced.get("settle_calls", 0), traced["steps"]
+
+    # per-step time of each kernel family on the 16,384-token head (same run, headline calls)
+    cfg = traced["config"]
+    base = {}
+    for fam, prefix, kind, per_cu in SHAPE_KERNELS:
+        nm = _shape_kernel_name(prefix, cfg["d"], cfg["causal"], names)
+        if nm is None or len(launches[nm]) < W + K:
+            continue
+        d_us = statistics.mean((e - s_) / 1e3 for s_, e in launches[nm][W:W + K])
+        tiles = (cfg["N"] + 127) // 128
+        target = {"statistics": 512, "pass 1": 256, "pass 2": 512}[fam]
+        spl = _auto_splits(cfg["B"] * cfg["H"], cfg["N"], target, tiles)
+        jobs = _dispatch_steps(kind, cfg["B"] * cfg["H"], cfg["N"], cfg["causal"], tiles, spl)
+        base[fam] = d_us / _makespan([j for j, _ in jobs], 256 * per_cu)
+
+    lines = ["# Kernel traces of the other shapes of the default bench run", "",
+             "Commands (repository root, one MI355X): the default bench run under the kernel tracer (the same run as "
+             "`profiles/long16k_kernel_trace.md`), then this digest.", "", "```",
+             "rocprofv3 --kernel-trace --stats -d <TRACE> -o run --output-format csv -- python3 bench.py > <TRACED_STDOUT>",
+             "python3 bench.py --digest-shapes <TRACE> <TRACED_STDOUT> " + os.path.relpath(out, ROOT), "```", "",
+             "Each shape's timed calls are the last launches of the kernels that only that shape uses. The dispatch "
+             "model lists every workgroup's 32-row steps in dispatch order (the kernels' own tile order: causal grids "
+             "heaviest tile first), places them greedily on the compute units' workgroup slots, and prices a step at "
+             "the per-step time of the same kernel on the 16,384-token head in the same run "
+             f"(statistics {base.get('statistics', float('nan')):.3f} us, pass 1 {base.get('pass 1', float('nan')):.3f} us, "
+             f"pass 2 {base.get('pass 2', float('nan')):.3f} us per step and slot). 'even' divides all steps evenly over "
+             "the slots; 'greedy' is the model's makespan; 'active' is the share of wave-steps whose wave has work "
+             "(causal diagonal tiles leave some of a workgroup's four waves waiting at its barriers).", ""]
+    summary = {}
+    for shape, oc in traced["other_configs"].items():
+        B, H, N, d, causal, calls = oc["B"], oc["H"], oc["N"], oc["d"], oc["causal"], oc["calls"]
+        bh = B * H
+        lines += [f"## {shape}: B={B}, H={H}, N={N}, d={d}, bf16, {'causal' if causal else 'non-causal'}", "",
+                  f"Bench line of the traced run: {oc['ms_per_call']} ms per call over {calls} calls.", "",
+                  "| Kernel | Launches | Average (us) | Min (us) | Max (us) | workgroups | splits | even (us) | "
+                  "greedy (us) | active | trace / greedy |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        total, spans, rec = 0.0, [], {}
+        first_last = []
+        for fam, prefix, kind, per_cu in SHAPE_KERNELS:
+            nm = _shape_kernel_name(prefix, d, causal, names)
+            if nm is None:
+                continue
+            ls = launches[nm][-calls:]
+            first_last.append(ls)
+            du = [(e - s_) / 1e3 for s_, e in ls]
+            avg = statistics.mean(du)
+            total += avg
+            q16 = "q16" in prefix
+            tiles = (N + 63) // 64 if q16 else (N + 127) // 128
+            slots = 256 * (1 if d == 128 else per_cu)
+            target = {"statistics": 512, "pass 1": 256, "pass 2": 256 * (2 if d == 64 else 1)}[fam]
+            spl = _auto_splits(bh, N, target, tiles)
+            jobs = _dispatch_steps(kind, bh, N, causal, tiles, spl)
+            steps = [j for j, _ in jobs]
+            act = sum(j * f for j, f in jobs) / max(1, sum(steps))
+            t_step = base.get(fam) if d == cfg["d"] and not q16 else None
+            even = sum(steps) / slots * t_step if t_step else None
+            greedy = _makespan(steps, slots) * t_step if t_step else None
+            fmt = lambda v, p=1: "—" if v is None else f"{v:.{p}f}"  # noqa: E731
+            lines.append(f"| `{nm}` | {len(du)} | {avg:.1f} | {min(du):.1f} | {max(du):.1f} | {len(jobs)} | {spl} | "
+                         f"{fmt(even)} | {fmt(greedy)} | {act:.3f} | {fmt(avg / greedy if greedy else None, 2)} |")
+            rec[fam] = {"kernel": nm, "launches": len(du), "avg_us": round(avg, 2), "workgroups": len(jobs),
+                        "splits": spl, "even_us": None if even is None else round(even, 2),
+                        "greedy_us": None if greedy is None else round(greedy, 2), "active_wave_steps": round(act, 4)}
+        span = statistics.mean((max(ls[i][1] for ls in first_last) - min(ls[i][0] for ls in first_last)) / 1e3
+                               for i in range(calls))
+        lines += ["", f"Sum of the kernel averages: {total:.1f} us per call; first launch start to last launch end: "
+                  f"{span:.1f} us per call (the difference is the gaps between launches).", ""]
+        summary[shape] = {"kernels": rec, "sum_of_kernel_avg_us": round(total, 2), "first_to_last_us": round(span, 2),
+                          "bench_ms_per_call": oc["ms_per_call"]}
+    lines += ["```json", json.dumps({"per_step_us_long16k": {k: round(v, 4) for k, v in base.items()},
+                                      "shapes": summary}, indent=1), "```", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {out}")
+
+
 def digest_trace(trace_dir, out, bench_log):
     """Summarise a rocprofv3 --kernel-trace run of the default `python3 bench.py`.
 
@@ -637,6 +820,8 @@ def main():
                     help="summarise pass 2's three split reductions (timing json + FETCH/WRITE runs per mode)")
     ap.add_argument("--digest-sq", nargs="+", metavar="OUT TRACE_DIR DIR=COUNTERS",
                     help="summarise rocprofv3 --pmc runs of matrix-core / issue counters into OUT (markdown)")
+    ap.add_argument("--digest-shapes", nargs=3, metavar=("TRACE_DIR", "BENCH_LOG", "OUT"),
+                    help="summarise the other shapes (other_configs) of a traced default run into OUT (markdown)")
     ap.add_argument("--digest-trace", nargs=3, metavar=("TRACE_DIR", "OUT", "BENCH_LOG"),
                     help="summarise a rocprofv3 --kernel-trace --stats run (csv dir) into OUT (markdown)")
     args = ap.parse_args()
@@ -645,6 +830,9 @@ def main():
         return
     if args.digest_trace:
         digest_trace(*args.digest_trace)
+        return
+    if args.digest_shapes:
+        digest_shapes(*args.digest_shapes)
         return
     if args.digest_sq:
         digest_sq(*args.digest_sq)

@@ -91,3 +91,27 @@ def test_trace_digest_selects_the_timed_launches(tmp_path, monkeypatch):
     assert summary["headline_region"]["kernels"]["bob_pass1"]["avg_us"] == (3000 + 100 * (W + 1)) / 1000
     assert summary["headline_region"]["kernels"]["attn_fwd_stats"]["launches"] == K
     assert abs(summary["roofline_region"]["frac_of_peak"] - 3.0e9 / (p1 * 1e-9) / 1e12 / 2500.0) < 1e-4
+
+
+def test_dispatch_model_of_causal_grids():
+    """The dispatch model behind the shape-trace digest: causal query tiles stream
+    (tile + 1) * 4 key steps, causal key tiles stream the queries from their own
+    tile on, and 10 of the 16 wave-steps of a diagonal 128 x 128 block have work."""
+    rows = bench._dispatch_steps("rows", 2, 512, True, 4, 1)
+    assert len(rows) == 8
+    assert sorted(j for j, _ in rows) == [4, 4, 8, 8, 12, 12, 16, 16]
+    assert [j for j, _ in rows][:2] == [16, 16]  # heaviest tile first, over all heads
+    cols = bench._dispatch_steps("cols", 2, 512, True, 4, 1)
+    assert [j for j, _ in cols][:2] == [16, 16] and sorted(j for j, _ in cols) == [4, 4, 8, 8, 12, 12, 16, 16]
+    for steps, frac in rows + cols:
+        q = steps // 4 - 1  # tiles before the diagonal one
+        assert abs(frac - (16 * q + 10) / (16 * q + 16)) < 1e-12
+    full = bench._dispatch_steps("rows", 1, 512, False, 4, 2)
+    assert [j for j, _ in full] == [8] * 8 and all(f == 1.0 for _, f in full)
+    # greedy placement in order: the longest job bounds the makespan
+    assert bench._makespan([32, 1, 1, 1], 2) == 32
+    assert bench._makespan([3, 3, 2, 2, 2], 2) == 7  # in order: (3, 3) (5, 3) (5, 5) (7, 5)
+    # the library's split rule: no split once the grid fills the target
+    assert bench._auto_splits(96, 1024, 256, 8) == 1
+    assert bench._auto_splits(1, 16384, 256, 128) == 2
+    assert bench._auto_splits(1, 16384, 512, 128) == 4
