@@ -85,19 +85,36 @@ __host__ __device__ constexpr int tpos(int k) { return (((k >> 2) & 1) << 4) + (
 // ---- LDS tile geometry --------------------------------------------------------
 // Row-major copy: 32 rows x D, row stride RS elements. For 16-bit types the rows
 // are unpadded and the 16-byte chunks of row r are stored XOR-swizzled: chunk c
-// at position c ^ swz(r). Measured on the MI355X with an LDS read microbenchmark
-// (16 lanes of a 16-byte read are served per cycle from 64 four-byte banks), the
-// swizzle (r / 2) mod 8 for 128-byte rows (d = 64) is as fast as a contiguous
-// read for the 16-byte row reads of the score operands and the fastest of the
-// layouts tried for the transposing 8-byte reads. 256-byte rows (d = 128) use
-// r mod 16 so that 16 consecutive rows read at one chunk hit 16 distinct
-// 16-byte bank groups. float32 rows are padded by one element instead.
+// at position c ^ swz(r), chosen so that the kernels' LDS reads are free of bank
+// conflicts (64 four-byte banks; rocprofv3 SQ_LDS_BANK_CONFLICT reads zero for the
+// statistics kernel and both passes at d = 64 and 128):
+//  - the 16-byte row reads of the score operands take 16 consecutive rows at one
+//    chunk, so the rows sharing a bank offset need distinct swizzles;
+//  - the transposing 8-byte reads take 4 aligned consecutive rows x 64 bytes
+//    (chunks 4m .. 4m + 3) per 32 lanes, so rows sharing a bank offset need
+//    swizzles that differ above bit 1.
+// d = 64 (128-byte rows: rows r and r + 1 are 32 banks apart): with h = (r / 2) mod 8,
+// swz = ((h & 1) << 2) | (h >> 1). d = 128 (256-byte rows, all at one bank offset):
+// swz = ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1), a bijection on 16
+// rows whose top two bits differ within every 4 aligned rows. The former swizzles,
+// (r / 2) mod 8 and r mod 16, left the transposing reads 2-way and 4-way
+// conflicted (23-60% of the LDS-active cycles).
+// Layout 1 is the 16-query d = 128 pass 1's own choice, r mod 16: its LDS conflicts
+// come from an access pattern the row swizzle does not change (the same count
+// under both), and it measured 2-3% faster with this one.
+// float32 rows are padded by one element instead.
 // Transposed copy (float32 kernels and the first backward): D rows (head dims)
 // x 32 columns in tpos() order, row stride TS.
-template <int D>
+template <int D, int L = 0>
 __device__ inline int swz(int row) {
-  if constexpr (D == 64) return (row >> 1) & 7;
-  return row & 15;
+  if constexpr (D == 64) {
+    const int h = (row >> 1) & 7;
+    return ((h & 1) << 2) | (h >> 1);
+  } else if constexpr (L == 1) {
+    return row & 15;
+  } else {
+    return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+  }
 }
 
 template <class TT, int D>
@@ -115,10 +132,10 @@ struct Geo {
 
 // Element offset of (row, col) in a row-major LDS tile (col: 4-element aligned
 // within its 16-byte chunk for 16-bit types).
-template <class TT, int D>
+template <class TT, int D, int L = 0>
 __device__ inline int roff(int row, int col) {
   if constexpr (sizeof(typename TT::elem) == 2) {
-    return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
+    return row * D + ((((col >> 3) ^ swz<D, L>(row)) << 3) | (col & 7));
   } else {
     return row * Geo<TT, D>::RS + col;
   }
@@ -239,7 +256,7 @@ __device__ inline void glds4(const void* gsrc, void* lds) {
 template <int D, int NWAVES>
 __host__ __device__ constexpr int stage_copies() { return kTile * (D / 8) / (64 * NWAVES); }
 
-template <class TT, int D, int NWAVES, bool ASYNC = false>
+template <class TT, int D, int NWAVES, bool ASYNC = false, int L = 0>
 __device__ inline void stage_direct(const typename TT::elem* __restrict__ src, int r0, int N,
                                     typename TT::elem* tile, int wave, int lane) {
   static_assert(sizeof(typename TT::elem) == 2, "16-bit types only");
@@ -251,7 +268,7 @@ __device__ inline void stage_direct(const typename TT::elem* __restrict__ src, i
     const int blk = p * NWAVES + wave;
     const int slot = blk * 64 + lane;
     const int row = slot / SPR, pc = slot % SPR;
-    const int c = pc ^ swz<D>(row);
+    const int c = pc ^ swz<D, L>(row);
     const int grow = min(r0 + row, N - 1);
     glds16<ASYNC>(src + (size_t)grow * D + c * 8, tile + blk * 64 * 8);
   }

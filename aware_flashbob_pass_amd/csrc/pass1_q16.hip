@@ -41,6 +41,7 @@ static constexpr int kQD = 128;
 static constexpr int kQTileElems = 32 * kQD;   // one 32-key row-major tile
 static constexpr int kQStageElems = 4 * kQTileElems;
 static constexpr int kQNBuf = 3;
+static constexpr int kQLayout = 1;  // LDS row swizzle of this kernel's tiles (common.hpp swz)
 
 template <class TT>
 __device__ inline f32x4 mfma_16x16x32(typename TT::vec a, typename TT::vec b, f32x4 c) {
@@ -61,8 +62,8 @@ __device__ inline typename TT::vec q16_tr_op(const typename TT::elem* tile, int 
   const int i = lane & 15, g = lane >> 4;
   const int col = mt * 16 + (i & 3) * 4;
   const int row = g * 4 + (i >> 2);
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + roff<TT, kQD>(row, col)));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + roff<TT, kQD>(row + 16, col)));
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + roff<TT, kQD, kQLayout>(row, col)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(tile + roff<TT, kQD, kQLayout>(row + 16, col)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename TT::vec, v);
@@ -71,7 +72,7 @@ __device__ inline typename TT::vec q16_tr_op(const typename TT::elem* tile, int 
 // A operand of a score product: key row m of the row-major tile, dims 32 ks + 8 g .. + 7.
 template <class TT>
 __device__ inline typename TT::vec q16_row_op(const typename TT::elem* tile, int m, int ks, int g) {
-  return *reinterpret_cast<const typename TT::vec*>(tile + roff<TT, kQD>(m, ks * 32 + g * 8));
+  return *reinterpret_cast<const typename TT::vec*>(tile + roff<TT, kQD, kQLayout>(m, ks * 32 + g * 8));
 }
 
 // gQ, gdO at dims 16 mt + 4 g .. + 3 of query qi.
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_q16_kernel(Pass1Args a) {
   auto issue = [&](int stg, int j) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      stage_direct<TT, kQD, kQWaves>(src[t], (kt_begin + j) * 32, N, lds + stg * kQStageElems + t * kQTileElems,
+      stage_direct<TT, kQD, kQWaves, false, kQLayout>(src[t], (kt_begin + j) * 32, N, lds + stg * kQStageElems + t * kQTileElems,
                                       wave, lane);
   };
   for (int j = 0; j < kQNBuf - 1 && j < nsteps; ++j) issue(j, j);
