@@ -99,9 +99,14 @@ __host__ __device__ constexpr int tpos(int k) { return (((k >> 2) & 1) << 4) + (
 // rows whose top two bits differ within every 4 aligned rows. The former swizzles,
 // (r / 2) mod 8 and r mod 16, left the transposing reads 2-way and 4-way
 // conflicted (23-60% of the LDS-active cycles).
-// Layout 1 is the 16-query d = 128 pass 1's own choice, r mod 16: its LDS conflicts
-// come from an access pattern the row swizzle does not change (the same count
-// under both), and it measured 2-3% faster with this one.
+// Layout 1 serves the 16-query d = 128 pass 1, whose reads group lanes differently
+// (16-byte row reads: 16 rows x 4 chunks per 64 lanes; transposing reads: 16 rows x
+// 32 bytes). No simple bank model predicted its conflicts, so its swizzle was found
+// by measurement: of 48 candidates (bit permutations of the row's low four bits,
+// with and without their low bits XOR-ed into the high ones), four read both
+// patterns without conflicts; this one is XOR-linear in the row bits
+// (8 b0 ^ 10 b1 ^ 5 b2 ^ 4 b3). They leave the 32-query kernels' transposing reads
+// 2-way conflicted, hence two layouts.
 // float32 rows are padded by one element instead.
 // Transposed copy (float32 kernels and the first backward): D rows (head dims)
 // x 32 columns in tpos() order, row stride TS.
@@ -111,7 +116,7 @@ __device__ inline int swz(int row) {
     const int h = (row >> 1) & 7;
     return ((h & 1) << 2) | (h >> 1);
   } else if constexpr (L == 1) {
-    return row & 15;
+    return ((row & 1) ? 8 : 0) ^ ((row & 2) ? 10 : 0) ^ ((row & 4) ? 5 : 0) ^ ((row & 8) ? 4 : 0);
   } else {
     return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
   }
