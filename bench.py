@@ -583,11 +583,14 @@ def digest_sq(out, trace_dir, *runs):
               f"{w_unit:.4g} flops; trace avg = the kernel-trace average of the same command. GRBM_GUI_ACTIVE "
               "sums the 8 XCDs, so the clock during the kernel is GRBM_GUI_ACTIVE / 8 / trace avg and the "
               "matrix cores' busy fraction is SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs). "
-              "SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_LDS count in the same unit, so their ratios "
-              "are fractions of the waves' resident time.", "",
+              "SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_LDS, SQ_WAIT_ANY (waiting at s_waitcnt) and "
+              "SQ_WAIT_INST_ANY (waiting to issue) count in the same unit, so their ratios are fractions of the "
+              "waves' resident time; SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE is the share of the LDS's busy "
+              "cycles lost to bank conflicts.", "",
               "| Kernel | MFMA flops / dispatch | counted / model | trace avg (us) | counted TFLOP/s | clock (GHz) | "
-              "MFMA busy | co-exec / MFMA busy | VALU active / wave | LDS wait / wave |",
-              "|---|---|---|---|---|---|---|---|---|---|"]
+              "MFMA busy | co-exec / MFMA busy | VALU active / wave | LDS wait / wave | waitcnt / wave | "
+              "issue wait / wave | LDS bank conflict / LDS active |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
 
     def mean(k, c):
         v = vals[k].get(c)
@@ -604,7 +607,10 @@ def digest_sq(out, trace_dir, *runs):
                      f"{cyc / t / 1e9:.2f} | {mean(k, 'SQ_VALU_MFMA_BUSY_CYCLES') / (cyc * 1024):.3f} | "
                      f"{mean(k, 'SQ_VALU_MFMA_COEXEC_CYCLES') / mean(k, 'SQ_VALU_MFMA_BUSY_CYCLES'):.3f} | "
                      f"{mean(k, 'SQ_ACTIVE_INST_VALU') / mean(k, 'SQ_WAVE_CYCLES'):.3f} | "
-                     f"{mean(k, 'SQ_WAIT_INST_LDS') / mean(k, 'SQ_WAVE_CYCLES'):.3f} |")
+                     f"{mean(k, 'SQ_WAIT_INST_LDS') / mean(k, 'SQ_WAVE_CYCLES'):.3f} | "
+                     f"{mean(k, 'SQ_WAIT_ANY') / mean(k, 'SQ_WAVE_CYCLES'):.3f} | "
+                     f"{mean(k, 'SQ_WAIT_INST_ANY') / mean(k, 'SQ_WAVE_CYCLES'):.3f} | "
+                     f"{mean(k, 'SQ_LDS_BANK_CONFLICT') / mean(k, 'SQ_LDS_IDX_ACTIVE'):.3f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
