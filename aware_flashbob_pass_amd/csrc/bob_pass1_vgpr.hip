@@ -4,23 +4,36 @@
 // tiles stay in AGPRs through inline-assembly products (mfma_acc). With the default
 // form a kernel of more than 256 registers puts every product in AGPRs, and each step
 // then copies its four score tiles out with v_accvgpr_read before the element-wise work.
+#include <cmath>
+
 #include "pass1_kernel.hpp"
 
 namespace fb {
 
-template <class TT, bool CAUSAL>
+template <class TT, bool CAUSAL, bool FOLD = false>
 static hipError_t launch_64(const Pass1Args& a, hipStream_t s) {
   const size_t lds = pass1_lds_bytes<TT, 64>();
-  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass>, lds);
+  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass>), dim3(row_tiles(a.N), a.BH, a.nsplit), dim3(kBlock),
-                     lds, s, a);
+  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD>), dim3(row_tiles(a.N), a.BH, a.nsplit),
+                     dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
+// tau folds exactly into bf16 operands when it is a positive power of two (bf16 has
+// float32's exponent range; 2^-60 .. 2^60 keeps any value above 2^-66 a normal number).
+static bool tau_folds(float tau) {
+  int e = 0;
+  return tau > 0.f && std::frexp(tau, &e) == 0.5f && e >= -59 && e <= 61;
+}
+
+// The non-causal sweep folds tau when it can (pass 1 347 -> 343 us at N = 16384, same
+// box); the causal one measured 1.5% slower folded and keeps the multiplication.
 hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s) {
   switch (dt) {
-    case DT::BF16: return causal ? launch_64<BF16, true>(a, s) : launch_64<BF16, false>(a, s);
+    case DT::BF16:
+      if (causal) return launch_64<BF16, true>(a, s);
+      return tau_folds(a.tau) ? launch_64<BF16, false, true>(a, s) : launch_64<BF16, false>(a, s);
     case DT::F16: return causal ? launch_64<F16, true>(a, s) : launch_64<F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }

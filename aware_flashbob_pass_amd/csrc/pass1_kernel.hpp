@@ -147,7 +147,11 @@ __host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
   return (mode == kTwoPass || (d == 128 && mode != kAlphaPass)) ? 1 : 2;
 }
 
-template <class TT, int D, bool CAUSAL, int MODE>
+// FOLD (two-pass sweep, bf16, tau a positive power of two): the resident Q and UQ
+// rows are scaled by tau once, which is exact, so the score products give tau S and
+// G = tau (UQ K^T + Q UK^T) directly (the same float32 values as scaling afterwards)
+// and each step saves the 16 multiplications of G by tau.
+template <class TT, int D, bool CAUSAL, int MODE, bool FOLD = false>
 __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
@@ -193,10 +197,20 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
   load_resident<TT, D>(reinterpret_cast<const T*>(a.dO) + base, qi, N, g, bdo);
   if constexpr (NEED_G) load_resident<TT, D>(reinterpret_cast<const T*>(a.UQ) + base, qi, N, g, buq);
+  static_assert(!FOLD || (MODE == kTwoPass && std::is_same_v<TT, BF16>), "tau folding: bf16 two-pass sweep only");
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int t = 0; t < DK; ++t)
+#pragma unroll
+      for (int s = 0; s < TT::KPL; ++s) {
+        bq[t][s] = TT::cvt(TT::tof(bq[t][s]) * a.tau);
+        buq[t][s] = TT::cvt(TT::tof(buq[t][s]) * a.tau);
+      }
+  }
   const size_t rowv = (size_t)bh * N + (qi < N ? qi : 0);
   const float lq = a.L[rowv] * kLog2e;
   const float dq = a.D[rowv];
-  const float cs = a.tau * kLog2e;
+  const float cs = FOLD ? kLog2e : a.tau * kLog2e;
   const float tau = a.tau;
   const float al = (MODE == kEnergyPass || MODE == kRowsPass) ? a.alpha[rowv] : 0.f;
   const float er = MODE == kRowsPass ? a.E[rowv] : 0.f;
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
       V wa[NK], wb[NK], pp[NK], pg[NK];
       auto elementwise = [&](int r) {
         const float p = fast_exp2(sc[r]);
-        const float gv = gc[r] * tau;
+        const float gv = FOLD ? gc[r] : gc[r] * tau;
         const int kk = r >> 3, ss = r & 7;
         if constexpr (MODE == kAlphaPass) {
           alpha_p += p * gv;
