@@ -10,12 +10,12 @@
 
 namespace fb {
 
-template <class TT, bool CAUSAL, bool FOLD = false>
+template <class TT, bool CAUSAL, bool FOLD = false, bool ASML = false>
 static hipError_t launch_64(const Pass1Args& a, hipStream_t s) {
-  const size_t lds = pass1_lds_bytes<TT, 64>();
-  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD>, lds);
+  const size_t lds = ASML ? pass1_asm_lds_bytes() : pass1_lds_bytes<TT, 64>();
+  hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD>), dim3(row_tiles(a.N), a.BH, a.nsplit),
+  hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>), dim3(row_tiles(a.N), a.BH, a.nsplit),
                      dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
@@ -33,7 +33,8 @@ hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t 
   switch (dt) {
     case DT::BF16:
       if (causal) return launch_64<BF16, true>(a, s);
-      return tau_folds(a.tau) ? launch_64<BF16, false, true>(a, s) : launch_64<BF16, false>(a, s);
+      if (!tau_folds(a.tau)) return launch_64<BF16, false>(a, s);
+      return a.N % 32 == 0 ? launch_64<BF16, false, true, true>(a, s) : launch_64<BF16, false, true>(a, s);
     case DT::F16: return causal ? launch_64<F16, true>(a, s) : launch_64<F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }

@@ -8,6 +8,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "pass1_asm.hpp"
 #include "pass1_common.hpp"
 
 namespace fb {
@@ -151,7 +152,10 @@ __host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
 // rows are scaled by tau once, which is exact, so the score products give tau S and
 // G = tau (UQ K^T + Q UK^T) directly (the same float32 values as scaling afterwards)
 // and each step saves the 16 multiplications of G by tau.
-template <class TT, int D, bool CAUSAL, int MODE, bool FOLD = false>
+// ASML (that sweep, non-causal, N a multiple of 32): the step loop runs as one
+// inline-assembly block with a fixed schedule (pass1_asm_steps) instead of the
+// compiled steps.
+template <class TT, int D, bool CAUSAL, int MODE, bool FOLD = false, bool ASML = false>
 __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
@@ -161,7 +165,8 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   // and awaited one step before use; d = 128 (no register room for the deeper
   // unroll) keeps three stages, two steps ahead, compiler-visible copies.
   constexpr bool DEEP = D == 64;
-  constexpr int NT = 4, NBUF = DEEP ? 4 : 3, AHEAD = NBUF - 1;
+  constexpr int NT = 4, NBUF = ASML ? FB_PASS1_ASM_SLOTS : DEEP ? 4 : 3;
+  constexpr int AHEAD = ASML ? FB_PASS1_ASM_AHEAD : NBUF - 1;
   // The two-pass sweeps keep their four accumulator tiles in AGPRs from inline
   // assembly and are compiled with the VGPR form for everything else
   // (bob_pass1_vgpr.hip), so the element-wise work reads the score tiles where the
@@ -482,9 +487,16 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
     if constexpr (MODE == kAlphaPass) asm volatile("" : "+v"(alpha_p)::"memory");
     if constexpr (MODE == kEnergyPass) asm volatile("" : "+v"(e0_p)::"memory");
   };
-  int j = 0;
-  for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
-  unroll_steps_until(step, j, nsteps, std::make_integer_sequence<int, NBUF - 1>{});
+  if constexpr (ASML) {
+    static_assert(FOLD && !CAUSAL && D == 64, "scheduled loop: folded non-causal d = 64");
+    const size_t ahead = (size_t)(kt_begin + AHEAD) * kTile * D;  // copy sources of step 0
+    pass1_asm_steps(sc, gc, pc, hc, bq, buq, bdo, accA, accB, accC, accX, alpha_p, e0_p, lq, dq, src[0] + ahead,
+                    src[1] + ahead, src[2] + ahead, src[3] + ahead, lds, wave, lane, nsteps);
+  } else {
+    int j = 0;
+    for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
+    unroll_steps_until(step, j, nsteps, std::make_integer_sequence<int, NBUF - 1>{});
+  }
 
   if constexpr (TWO) {
     if constexpr (ASM_ACC) pass1_acc_settle<MBA>(accA, accB, accC, accX);
@@ -502,6 +514,9 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
     fourpass_write_record<TT, D, MODE>(accA, accX, sp, split, bh, qt, wave, lane, a);
   }
 }
+
+// LDS of the scheduled loop: FB_PASS1_ASM_SLOTS stages of K, V, UK, UV.
+inline size_t pass1_asm_lds_bytes() { return (size_t)FB_PASS1_ASM_SLOTS * 4 * 32 * 64 * 2; }
 
 template <class TT, int D>
 inline size_t pass1_lds_bytes() {

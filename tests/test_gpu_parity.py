@@ -113,6 +113,19 @@ def test_bob_splits(splits, causal):
     _check_full(workload.custom(1, 2, 1000, 64, "bf16", causal), splits=splits)
 
 
+@pytest.mark.parametrize("N,splits", [(32, None), (64, None), (96, None), (128, None), (160, None), (192, None),
+                                      (224, None), (288, None), (1024, None), (1024, (3, 5)), (2048, (7, 2)),
+                                      (96, (5, 3))])
+def test_bob_scheduled_loop(N, splits):
+    """Non-causal bf16 at d = 64 with a power-of-two tau and N a multiple of 32: pass 1
+    runs its step loop as one inline-assembly block. Sweeps of 1 .. 9 steps cover the
+    four-step body and every tail length; splits give sweeps that start at a nonzero key
+    block, and more splits than key blocks give workgroups with no step at all."""
+    w = workload.custom(2, 2, N, 64, "bf16", False)
+    assert math.log2(w.scale).is_integer()
+    _check_full(w, splits=splits)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("splits", [(2, 3), (7, 5)])
