@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + qt) * 4 + wave;
   float* R = a.part + rec * fwd_record_floats(D);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) store_acc16(R + (mb * 64 + lane) * 16, acc[mb]);  // [MB][64 lanes][16]
+  for (int mb = 0; mb < MB; ++mb) store_tile16(R + mb * 1024, lane, acc[mb]);  // [MB] quad-major tiles
   R[MB * 16 * 64 + lane] = m;
   R[MB * 16 * 64 + 64 + lane] = l;
 }
@@ -215,9 +215,10 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
 // Merge the split records of one wave (fixed split order) and apply the epilogue.
 // A workgroup takes one wave's record (grid x = query tile x wave); the 8 threads
 // 8 n .. 8 n + 7 hold row n of it: record lanes n and n + 32 (g) times slots
-// 4 r4 .. 4 r4 + 3 of every head-dim block, so the loads are 16 contiguous bytes per
-// thread, four times as many waves are in flight as with one thread per record
-// lane, and D = dO . O of the row is summed over those 8 adjacent lanes.
+// 4 r4 .. 4 r4 + 3 of every head-dim block (quad-major tiles: for one r4, the 8 rows
+// of a wave read two runs of 128 contiguous bytes), four times as many waves are in
+// flight as with one thread per record lane, and D = dO . O of the row is summed
+// over those 8 adjacent lanes.
 template <class TT, int D, bool WITH_D>
 __global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
   using G = Geo<TT, D>;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kBlock) void attn_fwd_combine_kernel(FwdArgs a) {
     llo += w * R[MOFF + 64 + n];
     lhi += w * R[MOFF + 96 + n];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] += w * *reinterpret_cast<const f32x4*>(R + (mb * 64 + L) * 16 + r4 * 4);
+    for (int mb = 0; mb < MB; ++mb) acc[mb] += w * tile_quad(R + mb * 1024, L, r4);
   }
   const float lt = llo + lhi;
   const float inv = 1.f / lt;

@@ -179,12 +179,12 @@ __global__ __launch_bounds__(kBlock) void fourpass_combine_kernel(Pass1Args a) {
     const float* R = fourpass_record<TT, D, MODE>(a, sp, bh, blockIdx.x, wave);
     if constexpr (MODE == kDqPass) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) Q[mb] += load_acc16(R + (mb * 64 + lane) * 16);
+      for (int mb = 0; mb < MB; ++mb) Q[mb] += load_tile16(R + mb * 1024, lane);
     } else if constexpr (MODE == kRowsPass) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        Q[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-        X[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+        Q[mb] += load_tile16(R + (0 * MB + mb) * 1024, lane);
+        X[mb] += load_tile16(R + (1 * MB + mb) * 1024, lane);
       }
     } else {
       s_p += R[lane];
@@ -195,16 +195,17 @@ __global__ __launch_bounds__(kBlock) void fourpass_combine_kernel(Pass1Args a) {
 
 // Sum the split records of one wave in split order and apply the epilogue. A
 // workgroup takes one wave's record and one 32-wide head-dim block (grid x = query
-// tile x wave, z = block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of
-// record lane t / 4, so consecutive threads read consecutive 16 bytes and four times
-// as many waves are in flight as with one thread per record lane. The sums are
-// formed in the same order as in one-lane-per-thread form (split by split, then
-// the row's lane pair), and block 0 writes the row scalars.
+// tile x wave, z = block); thread t sums slots 4 (t / 64) .. 4 (t / 64) + 3 of
+// record lane t % 64, so consecutive threads read consecutive 16 bytes of the
+// quad-major record tiles and four times as many waves are in flight as with one
+// thread per record lane. The sums are formed in the same order as in
+// one-lane-per-thread form (split by split, then the row's lane pair), and block 0
+// writes the row scalars.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) {
   constexpr int MB = P1<TT, D>::MBA;
   constexpr int ACC = P1<TT, D>::ACC_FLOATS;
-  const int L = threadIdx.x >> 2, r4 = threadIdx.x & 3;
+  const int L = threadIdx.x & 63, r4 = threadIdx.x >> 6;
   const int g = L >> 5, n = L & 31;
   const int qt = blockIdx.x >> 2, wave = blockIdx.x & 3;
   const int bh = blockIdx.y, mbl = blockIdx.z;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void bob_pass1_combine_kernel(Pass1Args a) 
     const float* R = pass1_record<TT, D>(a, sp, bh, qt, wave);
     f32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(R + ((k * MB + mbl) * 64 + L) * 16 + r4 * 4);
+    for (int k = 0; k < 4; ++k) v[k] = tile_quad(R + (k * MB + mbl) * 1024, L, r4);
     alo += R[ACC + n];
     ahi += R[ACC + 32 + n];
     elo += R[ACC + 64 + n];

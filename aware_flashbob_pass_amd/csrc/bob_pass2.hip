@@ -151,13 +151,14 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_simple_kernel(Pass2Args a) {
 
 // Sum the split records of one wave in split order and write one 32-wide head-dim
 // block of gK, gV. A workgroup takes one wave's record and one block (grid x = key
-// tile x wave, z = block); thread t sums slots 4 (t % 4) .. 4 (t % 4) + 3 of record
-// lane t / 4, so consecutive threads read consecutive 16 bytes and four times as
-// many waves are in flight as with one thread per record lane.
+// tile x wave, z = block); thread t sums slots 4 (t / 64) .. 4 (t / 64) + 3 of record
+// lane t % 64, so consecutive threads read consecutive 16 bytes of the quad-major
+// record tiles and four times as many waves are in flight as with one thread per
+// record lane.
 template <class TT, int D>
 __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
   constexpr int MB = Geo<TT, D>::MB;
-  const int L = threadIdx.x >> 2, r4 = threadIdx.x & 3;
+  const int L = threadIdx.x & 63, r4 = threadIdx.x >> 6;
   const int g = L >> 5, n = L & 31;
   const int kt = blockIdx.x >> 2, wave = blockIdx.x & 3;
   const int bh = blockIdx.y, mb = blockIdx.z;
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(kBlock) void bob_pass2_reduce_kernel(Pass2Args a) {
   f32x4 dK = {0.f, 0.f, 0.f, 0.f}, dV = {0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < a.nsplit; ++sp) {
     const float* R = a.part + ((((size_t)sp * a.BH + bh) * kt_count + kt) * 4 + wave) * pass2_record_floats(D);
-    const f32x4 k4 = *reinterpret_cast<const f32x4*>(R + ((0 * MB + mb) * 64 + L) * 16 + r4 * 4);
-    const f32x4 v4 = *reinterpret_cast<const f32x4*>(R + ((1 * MB + mb) * 64 + L) * 16 + r4 * 4);
+    const f32x4 k4 = tile_quad(R + (0 * MB + mb) * 1024, L, r4);
+    const f32x4 v4 = tile_quad(R + (1 * MB + mb) * 1024, L, r4);
     dK += k4;
     dV += v4;
   }

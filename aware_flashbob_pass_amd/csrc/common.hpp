@@ -382,17 +382,24 @@ __device__ inline f32x16 zero16() {
   return z;
 }
 
-// One lane's 16 accumulator values as 4 x 16-byte global accesses.
-__device__ inline void store_acc16(float* dst, const f32x16& v) {
+// A wave's 16 accumulator slots per lane as one 1024-float record tile, quad-major:
+// slots 4q .. 4q + 3 of lane L at floats 4 (64 q + L). Each of the wave's four 16-byte
+// stores (or loads) of a tile then covers 1 KB of contiguous memory; with each lane's
+// 16 slots contiguous instead, every store was strided by 64 bytes per lane and the
+// split-record writes at the end of pass 1 ran at about a third of HBM's rate.
+__device__ inline void store_tile16(float* tile, int lane, const f32x16& v) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    reinterpret_cast<f32x4*>(dst)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    reinterpret_cast<f32x4*>(tile)[q * 64 + lane] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
-__device__ inline f32x16 load_acc16(const float* src) {
+__device__ inline f32x4 tile_quad(const float* tile, int lane, int q) {
+  return reinterpret_cast<const f32x4*>(tile)[q * 64 + lane];
+}
+__device__ inline f32x16 load_tile16(const float* tile, int lane) {
   f32x16 v;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(src)[q];
+    const f32x4 x = tile_quad(tile, lane, q);
     v[4 * q] = x[0];
     v[4 * q + 1] = x[1];
     v[4 * q + 2] = x[2];

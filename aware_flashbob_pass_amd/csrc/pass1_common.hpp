@@ -23,7 +23,8 @@ struct P1 {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
   static constexpr int MBA = G::MB;  // accumulated 32-wide head-dim blocks
-  // record layout (floats): acc[4][MBA][64 lanes][16], alpha_p[64], e0_p[64]
+  // record layout (floats): acc[4][MBA] tiles of [4 quads][64 lanes][4] (store_tile16),
+  // alpha_p[64], e0_p[64]
   static constexpr int ACC_FLOATS = 4 * MBA * 16 * 64;
 };
 
@@ -109,10 +110,10 @@ __device__ inline void pass1_write_record(const f32x16 (&A)[P1<TT, D>::MBA], con
   float* R = pass1_record<TT, D>(a, split, bh, qt, wave);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, A[mb]);
-    store_acc16(R + ((1 * MB + mb) * 64 + lane) * 16, B[mb]);
-    store_acc16(R + ((2 * MB + mb) * 64 + lane) * 16, C[mb]);
-    store_acc16(R + ((3 * MB + mb) * 64 + lane) * 16, X[mb]);
+    store_tile16(R + (0 * MB + mb) * 1024, lane, A[mb]);
+    store_tile16(R + (1 * MB + mb) * 1024, lane, B[mb]);
+    store_tile16(R + (2 * MB + mb) * 1024, lane, C[mb]);
+    store_tile16(R + (3 * MB + mb) * 1024, lane, X[mb]);
   }
   R[P1<TT, D>::ACC_FLOATS + lane] = alpha_p;
   R[P1<TT, D>::ACC_FLOATS + 64 + lane] = e0_p;

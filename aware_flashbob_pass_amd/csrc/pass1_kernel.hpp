@@ -86,12 +86,12 @@ __device__ inline void fourpass_write_record(const f32x16 (&Q)[D / 32], const f3
   float* R = fourpass_record<TT, D, MODE>(a, split, bh, qt, wave);
   if constexpr (MODE == kDqPass) {
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) store_acc16(R + (mb * 64 + lane) * 16, Q[mb]);
+    for (int mb = 0; mb < D / 32; ++mb) store_tile16(R + mb * 1024, lane, Q[mb]);
   } else if constexpr (MODE == kRowsPass) {
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      store_acc16(R + ((0 * (D / 32) + mb) * 64 + lane) * 16, Q[mb]);
-      store_acc16(R + ((1 * (D / 32) + mb) * 64 + lane) * 16, X[mb]);
+      store_tile16(R + (0 * (D / 32) + mb) * 1024, lane, Q[mb]);
+      store_tile16(R + (1 * (D / 32) + mb) * 1024, lane, X[mb]);
     }
   } else {
     R[lane] = s_p;

@@ -47,11 +47,11 @@ __device__ inline void pass2_write_record(const f32x16 (&dK)[Geo<TT, D>::MB], co
                                           int split, int bh, int kt, int wave, int lane, const Pass2Args& a) {
   constexpr int MB = Geo<TT, D>::MB;
   const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(a.N) + kt) * 4 + wave;
-  float* R = a.part + rec * pass2_record_floats(D);  // [2][MB][64 lanes][16]
+  float* R = a.part + rec * pass2_record_floats(D);  // [2][MB] quad-major tiles (store_tile16)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    store_acc16(R + ((0 * MB + mb) * 64 + lane) * 16, dK[mb]);
-    store_acc16(R + ((1 * MB + mb) * 64 + lane) * 16, dV[mb]);
+    store_tile16(R + (0 * MB + mb) * 1024, lane, dK[mb]);
+    store_tile16(R + (1 * MB + mb) * 1024, lane, dV[mb]);
   }
 }
 
@@ -108,8 +108,8 @@ __device__ inline void pass2_last_block_merge(int kt, int bh, int wave, int lane
         a.part + ((((size_t)sp * a.BH + bh) * row_tiles(a.N) + kt) * 4 + wave) * pass2_record_floats(D);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      dK[mb] += load_acc16(R + ((0 * MB + mb) * 64 + lane) * 16);
-      dV[mb] += load_acc16(R + ((1 * MB + mb) * 64 + lane) * 16);
+      dK[mb] += load_tile16(R + (0 * MB + mb) * 1024, lane);
+      dV[mb] += load_tile16(R + (1 * MB + mb) * 1024, lane);
     }
   }
   pass2_epilogue<TT, D>(dK, dV, kj, g, bh, a);
