@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     bob_attention_noalloc,
     bob_attention_with_stats,
     load_library,
+    probe_gq_atomics,
     profile_start,
     profile_stop,
     set_alloc_limit,

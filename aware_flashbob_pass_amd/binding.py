@@ -39,6 +39,7 @@ SIGNATURES = {
     "fb_set_tuning": (_I, [_I, _I]),
     "fb_set_alloc_limit": (_I, [_S]),
     "fb_set_reduction": (_I, [_I]),
+    "fb_probe_gq_atomics": (_I, [_P, _I, _I, _I, _I, _I, _P]),
     "fb_profile_start": (None, [ctypes.c_char_p]),
     "fb_profile_stop": (_I, [ctypes.POINTER(KernelTime), _I]),
 }
@@ -123,6 +124,15 @@ def set_reduction(mode=0):
     """Pass 2's split reduction: 0 records + merge kernel, 1 float32 atomics, 2 last
     workgroup merges (see fb_set_reduction in flashbob.h)."""
     _check(load_library().fb_set_reduction(int(mode)))
+
+
+def probe_gq_atomics(gq, B, H, N, d, splits):
+    """Measurement probe: the float32 atomic additions of a schedule that forms gQ in
+    pass 2 (see fb_probe_gq_atomics in flashbob.h). gq: [B][H][N][d] float32 on the GPU;
+    every element grows by ceil(N / 128)."""
+    if gq.dtype != torch.float32 or not gq.is_cuda or gq.numel() != B * H * N * d or not gq.is_contiguous():
+        raise ValueError("gq must be a contiguous float32 GPU tensor of B*H*N*d elements")
+    _check(load_library().fb_probe_gq_atomics(_ptr(gq), B, H, N, d, splits, _stream()))
 
 
 def set_alloc_limit(nbytes=0):

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libflashbob.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd.hip", "bob_pass1.hip", "bob_pass1_vgpr.hip", "pass1_q16.hip", "bob_pass2.hip", "bob_pass2_vgpr.hip",
-           "attn_bwd.hip", "api.cpp"]
+           "attn_bwd.hip", "probes.hip", "api.cpp"]
 
 # Packed fp32 VALU ops are disabled: the kernels are written with scalar fp32
 # element-wise math and must not be auto-vectorised into v_pk_* forms.

@@ -375,6 +375,16 @@ fb_status_t fb_set_reduction(int mode) {
   return ok();
 }
 
+fb_status_t fb_probe_gq_atomics(float* gq, int B, int H, int N, int d, int splits, hipStream_t stream) {
+  fb_status_t st = check_shape(B, H, N, d, FB_BF16, 1.f);
+  if (st) return st;
+  if (splits < 1 || splits > kMaxSplits) return fail(FB_ERR_ARG, "splits=%d not in [1, %d]", splits, kMaxSplits);
+  if ((st = check_ptrs({{"gq", gq}}, 16))) return st;
+  st = run("probe_gq_atomics", stream, [&] { return fb::launch_probe_gq_atomics(gq, B * H, N, d, splits, stream); });
+  if (st) return st;
+  return ok();
+}
+
 fb_status_t fb_set_alloc_limit(size_t bytes) {
   g_alloc_limit.store(bytes);
   return ok();

@@ -91,6 +91,8 @@ hipError_t launch_pass1(const Pass1Args& a, DT dt, int d, bool causal, hipStream
 // translation unit; called by launch_pass1).
 hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s);
 hipError_t launch_pass1_combine(const Pass1Args& a, DT dt, int d, hipStream_t s);
+// Measurement probe (probes.hip): the float32 atomic additions of a gQ-in-pass-2 schedule.
+hipError_t launch_probe_gq_atomics(float* gq, int BH, int N, int d, int nsplit, hipStream_t s);
 // Pass 1 with 16-query waves for 16-bit inputs at d = 128 (64 queries per workgroup,
 // every score tile computed once) and its split merge.
 __host__ __device__ inline int pass1_q16_tiles(int N) { return (N + 63) / 64; }

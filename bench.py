@@ -654,6 +654,79 @@ def cpu_baseline(w, inputs, budget_s):
     }
 
 
+def alt_schedule_probe(args):
+    """Decide the alternative schedule by measurement: forming gQ in pass 2 would remove
+    pass 1's four gQ accumulating units (W_a UK, W_b K, W_a K, P K: 4 of its 11) and
+    shrink its split merge, but pass 2 would have to add every (key tile, query tile)
+    pair's 32 x d tile of gQ into float32 gQ with atomics. The probe kernel issues
+    exactly those additions with pass 2's grid and split count and nothing else, so its
+    time bounds the schedule's extra cost from below (the two extra accumulating units
+    of pass 2 and its weight transposes are not counted); if the atomics hid entirely
+    under pass 2's own work, pass 2 would still take at least the probe's time. The
+    saving is bounded from above by 4/11 of pass 1 plus its whole merge kernel."""
+    import torch
+
+    import aware_flashbob_pass_amd as fb
+    import workload
+
+    w = workload.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in workload.make_inputs(w, args.seed).items()}
+    ws = torch.empty(max(1, fb.workspace_bytes(w.B, w.H, w.N, w.d, w.torch_dtype)), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(g["Q"]) for _ in range(4)]
+
+    def step():
+        fb.bob_attention(g["Q"], g["K"], g["V"], g["dO"], g["UQ"], g["UK"], g["UV"], tau=w.scale, causal=w.causal,
+                         workspace=ws, out=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + args.settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    kern = {}
+    for name in ("bob_pass1", "bob_pass1_combine", "bob_pass2", "bob_pass2_reduce"):
+        fb.profile_start(name)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        for k, (n, t) in fb.profile_stop().items():
+            kern[k] = t / n
+    bh = w.B * w.H
+    tiles = (w.N + 127) // 128
+    s2 = _auto_splits(bh, w.N, (2 if w.d == 64 else 1) * 256, tiles)  # pass 2's default split count
+    gq = torch.zeros(bh * w.N * w.d, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        fb.probe_gq_atomics(gq, w.B, w.H, w.N, w.d, s2)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        fb.probe_gq_atomics(gq, w.B, w.H, w.N, w.d, s2)
+    stop.record()
+    torch.cuda.synchronize()
+    probe_ms = start.elapsed_time(stop) / args.steps
+    counted = bool(torch.all(gq == float((args.warmup + args.steps) * tiles)).item())
+    adds = bh * tiles * w.N * w.d
+    saving = kern.get("bob_pass1", 0.0) * 4 / 11 + kern.get("bob_pass1_combine", 0.0)
+    print(json.dumps({
+        "metric": "alternative schedule (gQ in pass 2 with float32 atomics): atomics alone vs the most it saves",
+        "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "pass2_splits": s2,
+        "atomic_adds_per_call": adds, "probe_gq_atomics_ms": round(probe_ms, 4),
+        "atomic_adds_per_ns": round(adds / (probe_ms * 1e6), 2), "probe_counts_exact": counted,
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "saving_upper_bound_ms": round(saving, 4),
+        # atomics serialised after pass 2's work, and (second figure) hidden under it as
+        # far as possible: pass 2 then takes at least the longer of the two
+        "alternative_slower_by_at_least_ms": round(probe_ms - saving, 4),
+        "alternative_slower_by_at_least_ms_if_overlapped": round(
+            max(0.0, probe_ms - kern.get("bob_pass2", 0.0)) - saving, 4),
+    }), flush=True)
+
+
 def hutchinson_bench(args, name):
     """One Hutchinson sample of the attention Hessian diagonal, diag(H) ~ u * (H u)
     with Rademacher u, where H is the Hessian of <dO, O(Q, K, V)> in (Q, K, V):
@@ -804,6 +877,8 @@ def main():
                     help="skip the untimed pass with HIP events around every kernel (the kernels field is then empty)")
     ap.add_argument("--hutchinson", action="store_true",
                     help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
+    ap.add_argument("--alt-schedule-probe", action="store_true",
+                    help="time the float32 atomics a gQ-in-pass-2 schedule needs against the pass-1 work it saves")
     ap.add_argument("--reduction", type=int, choices=(0, 1, 2), default=0,
                     help="pass 2's split reduction: 0 records + merge kernel, 1 float32 atomics, "
                          "2 last-workgroup merge (fb_set_reduction)")
@@ -881,6 +956,9 @@ def main():
         return
     if args.hutchinson:
         hutchinson_bench(args, "gpt2_hessian" if args.workload == "long_16k" else args.workload)
+        return
+    if args.alt_schedule_probe:
+        alt_schedule_probe(args)
         return
     w = workload.WORKLOADS[args.workload]
     fb.set_reduction(args.reduction)

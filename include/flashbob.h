@@ -205,6 +205,22 @@ fb_status_t fb_set_tuning(int pass1_splits, int pass2_splits);
 fb_status_t fb_set_reduction(int mode);
 
 /*
+ * fb_probe_gq_atomics: a measurement probe, not part of the BoB path. It issues the
+ * float32 atomic additions that a schedule forming gQ in pass 2 (instead of pass 1,
+ * the alternative to the review page's two-pass design, Summary) needs at the least:
+ * for every pair of a 128-key tile and a 32-query tile, one 32 x d tile of additions
+ * into gq (the four waves of the key tile having summed theirs first), each adding
+ * 1.0f, with pass 2's grid (key tiles x B*H x `splits`, split s taking its share of
+ * the query tiles in order) and no other arithmetic. Its time bounds from below what
+ * the atomics alone would cost that schedule.
+ * gq: device, [B][H][N][d] float32, 16-byte aligned, caller-owned; on completion
+ * (stream-ordered) every element has grown by ceil(N / 128).
+ * Errors: FB_ERR_SHAPE / FB_ERR_HEADDIM as bob_attention; FB_ERR_ARG for splits
+ * outside [1, 64]; FB_ERR_NULL for a NULL gq; FB_ERR_HIP for launch errors.
+ */
+fb_status_t fb_probe_gq_atomics(float* gq, int B, int H, int N, int d, int splits, hipStream_t stream);
+
+/*
  * fb_set_alloc_limit: process-wide cap, in bytes, on each device allocation the
  * library makes itself (bob_attention's workspace, attn_bwd's scratch); 0 (the
  * default) means no cap. A larger request returns FB_ERR_OOM before any HIP

@@ -31,6 +31,7 @@ hipError_t launch_zero_f32(float*, size_t, hipStream_t) { return hipErrorInvalid
 FB_STUB(launch_bwd_rowdot(const BwdArgs&, DT, int, int, hipStream_t))
 FB_STUB(launch_bwd_dq(const BwdArgs&, DT, int, bool, int, hipStream_t))
 FB_STUB(launch_bwd_dkdv(const BwdArgs&, DT, int, bool, int, hipStream_t))
+FB_STUB(launch_probe_gq_atomics(float*, int, int, int, int, hipStream_t))
 #undef FB_STUB
 }  // namespace fb
 
@@ -82,6 +83,14 @@ int main() {
     EXPECT(bob_workspace_bytes(1, 1, INT_MAX - 255, 128, FB_F16) > 0);
   }
   EXPECT(fb_set_reduction(0) == FB_OK);
+  // the measurement probe: argument checks, then the (stubbed) launch
+  {
+    alignas(16) float gq[4];
+    EXPECT(fb_probe_gq_atomics(nullptr, 1, 1, 256, 64, 1, nullptr) == FB_ERR_NULL);
+    EXPECT(fb_probe_gq_atomics(gq, 1, 1, 256, 64, 0, nullptr) == FB_ERR_ARG);
+    EXPECT(fb_probe_gq_atomics(gq, 1, 1, INT_MAX, 64, 1, nullptr) == FB_ERR_SHAPE);
+    EXPECT(fb_probe_gq_atomics(gq, 1, 1, 256, 64, 1, nullptr) == FB_ERR_HIP);
+  }
   EXPECT(fb_set_tuning(0, 0) == FB_OK);
 
   // argument checks of the workspace entry point

@@ -138,6 +138,16 @@ def test_other_entry_point_checks(lib):
     assert st == FB_ERR_ARG
 
 
+def test_probe_argument_checks(lib):
+    """The measurement probe checks its arguments before any launch."""
+    dummy = ctypes.c_void_p(16)
+    assert lib.fb_probe_gq_atomics(None, 1, 1, 256, 64, 1, None) == FB_ERR_NULL
+    assert lib.fb_probe_gq_atomics(dummy, 1, 1, 256, 96, 1, None) == FB_ERR_HEADDIM
+    assert lib.fb_probe_gq_atomics(dummy, 1, 0, 256, 64, 1, None) == FB_ERR_SHAPE
+    for bad in (0, 65):
+        assert lib.fb_probe_gq_atomics(dummy, 1, 1, 256, 64, bad, None) == FB_ERR_ARG
+
+
 def test_size_overflow_bounds(lib):
     """B*H*N beyond 2^31 - 256 is rejected (row tile counts and launch ids are int);
     sizes just inside the bound give a finite, linear workspace without overflow."""

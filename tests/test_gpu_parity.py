@@ -439,6 +439,19 @@ def test_fourpass_matches_oracle(dtype, d, causal, N, splits):
 
 
 # ---- pass 2's split reduction (fb_set_reduction) -------------------------------
+@pytest.mark.parametrize("B,H,N,d,splits", [(1, 2, 300, 64, 3), (2, 1, 1000, 128, 1), (1, 1, 33, 64, 5)])
+def test_probe_gq_atomics_counts(B, H, N, d, splits):
+    """The measurement probe adds exactly one 1.0 per element for every 128-key tile."""
+    fb = _fb()
+    _note(f"case probe B={B} H={H} N={N} d={d} splits={splits}")
+    gq = torch.zeros(B * H * N * d, dtype=torch.float32, device="cuda")
+    fb.probe_gq_atomics(gq, B, H, N, d, splits)
+    fb.probe_gq_atomics(gq, B, H, N, d, splits)
+    torch.cuda.synchronize()
+    want = 2.0 * ((N + 127) // 128)
+    assert torch.all(gq == want).item(), (float(gq.min()), float(gq.max()), want)
+
+
 @pytest.mark.parametrize("dtype,d,causal,splits", [("bf16", 64, False, (2, 3)), ("bf16", 64, True, (3, 5)),
                                                    ("fp16", 64, False, (1, 8)), ("bf16", 128, False, (2, 3)),
                                                    ("bf16", 128, True, (7, 5)), ("fp16", 128, False, (2, 64))])
