@@ -33,7 +33,8 @@ UNITS = {"stats": 2, "pass1": 11, "pass2": 8, "exec": 21, "two_pass": 19, "usefu
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "bob_pass1_long16k_pmc.json")
 TRACE_SUMMARY = os.path.join(ROOT, "profiles", "long16k_kernel_trace.md")
 TRACE_JSON = os.path.join(ROOT, "profiles", "long16k_kernel_trace.json")
-PASS1_SOURCES = ("bob_pass1_vgpr.hip", "pass1_kernel.hpp", "pass1_common.hpp", "common.hpp", "kernels.hpp")
+PASS1_SOURCES = ("bob_pass1_vgpr.hip", "pass1_kernel.hpp", "pass1_asm.hpp", "pass1_asm_loop.inc", "pass1_common.hpp",
+                 "common.hpp", "kernels.hpp")
 # library kernel names (fb_profile_start) of one call, in launch order
 KERNELS_PER_CALL = {
     "two_pass": ("attn_fwd_stats", "attn_fwd_combine", "bob_pass1", "bob_pass1_combine", "bob_pass2",
@@ -45,7 +46,7 @@ KERNELS_PER_CALL = {
 TRACE_KERNELS = {
     "attn_fwd_stats": "attn_fwd_kernel<fb::BF16, 64, false, true>",
     "attn_fwd_combine": "attn_fwd_combine_kernel<fb::BF16, 64, true>",
-    "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0, true>",
+    "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0, true, true>",
     "bob_pass1_combine": "bob_pass1_combine_kernel<fb::BF16, 64>",
     "bob_pass2": "bob_pass2_kernel<fb::BF16, 64, false, false>",
     "bob_pass2_reduce": "bob_pass2_reduce_kernel<fb::BF16, 64>",
