@@ -655,6 +655,54 @@ def cpu_baseline(w, inputs, budget_s):
     }
 
 
+def microbench(out_md):
+    """Build and run the microbenchmarks and skeleton kernels of
+    aware_flashbob_pass_amd/csrc/microbench/probes_gen.py (one HIP program, generated
+    into a temporary directory) and print their figures as one JSON line; with a path,
+    also write them as a summary."""
+    import importlib.util
+    import subprocess
+    import tempfile
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    gen = os.path.join(here, "aware_flashbob_pass_amd", "csrc", "microbench", "probes_gen.py")
+    spec = importlib.util.spec_from_file_location("probes_gen", gen)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with tempfile.TemporaryDirectory() as tmp:
+        src, exe = os.path.join(tmp, "microbench_probes.hip"), os.path.join(tmp, "microbench_probes")
+        with open(src, "w") as fh:
+            fh.write(mod.render())
+        hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+        cmd = [hipcc, "-O3", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               src, "-o", exe]
+        log("microbench: building")
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise SystemExit(f"microbench build failed:\n{res.stderr[-2000:]}")
+        log("microbench: running")
+        run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    figures = {}
+    for line in run.stdout.splitlines():
+        name, _, rest = line.partition(": ")
+        parts = rest.split()
+        if name != "status" and parts:
+            figures[name] = {"value": float(parts[0]), "unit": " ".join(parts[1:])}
+    status = next((l.split(": ", 1)[1] for l in run.stdout.splitlines() if l.startswith("status: ")), "missing")
+    if run.returncode != 0 or status != "no error":
+        raise SystemExit(f"microbench run failed (rc {run.returncode}, status {status}):\n{run.stdout}\n{run.stderr}")
+    print(json.dumps({"microbench": figures}), flush=True)
+    if out_md:
+        rows = "\n".join(f"| `{k}` | {v['value']:g} | {v['unit']} |" for k, v in figures.items())
+        text = (f"# Microbenchmarks and skeleton kernels (one MI355X)\n\n"
+                f"Command (repository root): `python3 bench.py --microbench {out_md}`, which generates\n"
+                f"`microbench_probes.hip` from `aware_flashbob_pass_amd/csrc/microbench/probes_gen.py` (its\n"
+                f"docstring describes every probe), builds it with hipcc and runs it.\n\n"
+                f"| Probe | Value | Unit |\n|---|---|---|\n{rows}\n")
+        with open(out_md, "w") as fh:
+            fh.write(text)
+
+
 def alt_schedule_probe(args):
     """Decide the alternative schedule by measurement: forming gQ in pass 2 would remove
     pass 1's four gQ accumulating units (W_a UK, W_b K, W_a K, P K: 4 of its 11) and
@@ -878,6 +926,8 @@ def main():
                     help="skip the untimed pass with HIP events around every kernel (the kernels field is then empty)")
     ap.add_argument("--hutchinson", action="store_true",
                     help="time one Hutchinson Hessian-diagonal sample u * (H u) instead (default shape: gpt2_hessian)")
+    ap.add_argument("--microbench", nargs="?", const="", default=None, metavar="OUT_MD",
+                    help="build and run the microbenchmarks and skeleton kernels (optionally write a summary)")
     ap.add_argument("--alt-schedule-probe", action="store_true",
                     help="time the float32 atomics a gQ-in-pass-2 schedule needs against the pass-1 work it saves")
     ap.add_argument("--reduction", type=int, choices=(0, 1, 2), default=0,
@@ -960,6 +1010,9 @@ def main():
         return
     if args.alt_schedule_probe:
         alt_schedule_probe(args)
+        return
+    if args.microbench is not None:
+        microbench(args.microbench)
         return
     w = workload.WORKLOADS[args.workload]
     fb.set_reduction(args.reduction)
