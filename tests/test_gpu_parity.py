@@ -126,6 +126,17 @@ def test_bob_scheduled_loop(N, splits):
     _check_full(w, splits=splits)
 
 
+@pytest.mark.parametrize("tau", [0.25, 1.0, 2.0 ** -10, 2.0 ** -59, 2.0 ** -60, 2.0 ** 4, -0.125])
+def test_bob_scheduled_loop_tau(tau):
+    """The scheduled loop folds tau into the resident bf16 rows: powers of two from the
+    smallest folded one (2^-59) up, next to cases that keep the compiled loop (2^-60,
+    just outside the folding range, and a negative tau). Q and UQ are scaled by
+    1 / (8 |tau|) (a power of two, so exact in bf16) so that tau S and G have unit scale
+    as with the default tau, and every case is as well conditioned as the default."""
+    sig = 1.0 / (8.0 * abs(tau))
+    _check_full(workload.custom(1, 2, 256, 64, "bf16", False, sigma={"Q": sig, "UQ": sig}, tau=tau))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("splits", [(2, 3), (7, 5)])
