@@ -10,9 +10,9 @@
 
 namespace fb {
 
-template <class TT, bool CAUSAL, bool FOLD = false, bool ASML = false>
+template <class TT, bool CAUSAL, bool FOLD = false, int ASML = kAsmNone>
 static hipError_t launch_64(const Pass1Args& a, hipStream_t s) {
-  const size_t lds = ASML ? pass1_asm_lds_bytes() : pass1_lds_bytes<TT, 64>();
+  const size_t lds = ASML != kAsmNone ? pass1_asm_lds_bytes() : pass1_lds_bytes<TT, 64>();
   hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>), dim3(row_tiles(a.N), a.BH, a.nsplit),
@@ -27,14 +27,15 @@ static bool tau_folds(float tau) {
   return tau > 0.f && std::frexp(tau, &e) == 0.5f && e >= -59 && e <= 61;
 }
 
-// The non-causal sweep folds tau when it can (pass 1 347 -> 343 us at N = 16384, same
-// box); the causal one measured 1.5% slower folded and keeps the multiplication.
+// bf16 with a foldable tau runs the scheduled loop: over the whole sweep when no step
+// needs a mask (non-causal, N a multiple of 32), else over the steps that need none,
+// with compiled steps for the rest; other tau keep the compiled loop.
 hipError_t launch_pass1_d64(const Pass1Args& a, DT dt, bool causal, hipStream_t s) {
   switch (dt) {
     case DT::BF16:
-      if (causal) return launch_64<BF16, true>(a, s);
-      if (!tau_folds(a.tau)) return launch_64<BF16, false>(a, s);
-      return a.N % 32 == 0 ? launch_64<BF16, false, true, true>(a, s) : launch_64<BF16, false, true>(a, s);
+      if (!tau_folds(a.tau)) return causal ? launch_64<BF16, true>(a, s) : launch_64<BF16, false>(a, s);
+      if (causal) return launch_64<BF16, true, true, kAsmPrefix>(a, s);
+      return a.N % 32 == 0 ? launch_64<BF16, false, true, kAsmAll>(a, s) : launch_64<BF16, false, true, kAsmPrefix>(a, s);
     case DT::F16: return causal ? launch_64<F16, true>(a, s) : launch_64<F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }

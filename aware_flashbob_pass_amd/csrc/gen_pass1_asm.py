@@ -34,8 +34,9 @@ a[0:127] the accumulators (A, B, C, X at 0, 32, 64, 96; + 16 mb), a[128:175] the
 resident tau Q, tau UQ, dO operands (k-step t at 128 + 12 t, + 4, + 8), a[176:207] two
 buffers of score operands (K, V, UK, UV rows), a[208:239] two buffers of transposed
 operands (K^T, UK^T, V^T, UV^T). SGPRs: s[40:47] the copy sources of K, V, UK, UV (row
-block of step j + AHEAD), s48 the wave's LDS base, s50 the step index, s51 the step
-count, s52 scratch, s53 log2(e), s54 the caller's m0.
+block of step j + AHEAD), s48 the wave's LDS base, s49 the steps of the whole sweep (the
+copies run ahead to its end, also past the block's last step), s50 the step index, s51
+the block's step count, s52 scratch, s53 log2(e), s54 the caller's m0.
 
 Options kept for measurement (all produce the same results): the LDS operands in VGPRs
 (OPERANDS = "v"; no faster), more LDS stages and a longer copy distance (NBUF, AHEAD;
@@ -43,6 +44,7 @@ no faster: the copies land in time), no -D seed, other work splits.
 """
 
 import os
+import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "pass1_asm_loop.inc")
@@ -329,7 +331,7 @@ def step_text(S, label):
     """One complete step: guarded copies, the body, the copy wait and the barrier."""
     ins = []
     ins.append("s_add_u32 s52, s50, %d" % AHEAD)
-    ins.append("s_cmp_lt_u32 s52, s51")
+    ins.append("s_cmp_lt_u32 s52, s49")
     ins.append(f"s_cbranch_scc0 L_nocopy_{label}_%=")
     sc = (S + AHEAD) % NBUF
     for k in range(4):
@@ -342,7 +344,7 @@ def step_text(S, label):
         ins.append(f"s_add_u32 s{40 + 2 * k}, s{40 + 2 * k}, {TILE_BYTES}")
         ins.append(f"s_addc_u32 s{41 + 2 * k}, s{41 + 2 * k}, 0")
     ins.append("s_add_u32 s52, s50, %d" % AHEAD)
-    ins.append("s_cmp_lt_u32 s52, s51")
+    ins.append("s_cmp_lt_u32 s52, s49")
     ins.append(f"s_cbranch_scc0 L_wait0_{label}_%=")
     # the copies of step j + 2 (read from step j + 1 on) have landed; those of the
     # AHEAD - 2 latest steps may stay in flight
@@ -393,11 +395,33 @@ def loop_text():
     return ins
 
 
+def written_registers(ins):
+    """The VGPRs and AGPRs the instructions write (their first operand), as sorted lists."""
+    out = {"v": set(), "a": set()}
+    for x in ins:
+        op = x.split()[0]
+        if not (op.startswith("v_") or op.startswith("ds_read")):
+            continue
+        dst = x.split(None, 1)[1].split(",")[0].strip()
+        m = re.fullmatch(r"([va])(\d+)", dst) or re.fullmatch(r"([va])\[(\d+):(\d+)\]", dst)
+        if m:
+            lo = int(m.group(2))
+            hi = int(m.group(3)) if m.lastindex == 3 else lo
+            out[m.group(1)].update(range(lo, hi + 1))
+    return sorted(out["v"]), sorted(out["a"])
+
+
+# Registers bound to the block's outputs (the compiler knows they change): the score tiles,
+# the row sums and the accumulators. Every other register the block writes is a clobber.
+BOUND_V = set(range(0, 64)) | {254, 255}
+BOUND_A = set(range(0, 128))
+
+
 def render():
     ins = loop_text()
-    clob = ", ".join(f'"v{r}"' for r in range(64, 243))
-    if OPERANDS == "a":
-        clob += ", " + ", ".join(f'"a{r}"' for r in range(176, 240))
+    wv, wa = written_registers(ins)
+    assert not set(wv) & set(range(243, 254)) and not set(wa) & set(range(128, 176)), "block writes an input"
+    clob = ", ".join([f'"v{r}"' for r in wv if r not in BOUND_V] + [f'"a{r}"' for r in wa if r not in BOUND_A])
     clob += ', "s50", "s52", "s53", "s54", "scc", "memory"'
     return ("// Generated by gen_pass1_asm.py (same directory); do not edit by hand.\n"
             "// The step loop of pass 1's non-causal d = 64 bf16 sweep with tau folded: the\n"
@@ -406,6 +430,7 @@ def render():
             "#define FB_PASS1_ASM_LOOP \\\n" + " \\\n".join(f'  "{x}\\n\\t"' for x in ins) + "\n"
             "#define FB_PASS1_ASM_CLOBBERS " + clob + "\n"
             f"#define FB_PASS1_ASM_SLOTS {NBUF}\n"
+            f"#define FB_PASS1_ASM_DBIAS {int(DBIAS)}\n"
             f"#define FB_PASS1_ASM_AHEAD {AHEAD}\n")
 
 

@@ -76,6 +76,24 @@ __host__ __device__ inline size_t fwd_record_floats(int d) { return (size_t)((d 
 __host__ __device__ inline size_t pass2_record_floats(int d) { return (size_t)(2 * (d / 32) * 16) * 64; }
 __host__ __device__ inline int row_tiles(int N) { return (N + kBlockRows - 1) / kBlockRows; }
 
+// Steps of pass 1's scheduled block (the d = 64 bf16 sweep with tau folded) for the
+// workgroup of query tile qt sweeping key blocks [kt_begin, kt_begin + nsteps) of 32
+// keys, with `slots` LDS stages and copies `ahead` steps ahead. The block takes steps
+// that need no mask: key blocks before the workgroup's first query (causal) and whole
+// blocks of 32 keys. Its direct copies do not clamp rows past N, so none of them may
+// reach a ragged last block either: the block stops `ahead` steps before it, and the
+// compiled steps, whose copies clamp, issue that block's copy. It runs every step when
+// none needs a mask, else a multiple of `slots` so the compiled steps start at stage 0.
+__host__ __device__ inline int pass1_asm_step_count(int N, bool causal, int qt, int kt_begin, int nsteps, int slots,
+                                                    int ahead) {
+  const int whole = N / 32;  // whole 32-key blocks
+  int n = nsteps;
+  if (causal) n = qt * (kBlockRows / 32) - kt_begin;
+  if (whole < kt_begin + nsteps) n = n < whole - kt_begin - ahead ? n : whole - kt_begin - ahead;  // ragged block
+  n = n < 0 ? 0 : (n > nsteps ? nsteps : n);
+  return n == nsteps ? nsteps : n / slots * slots;
+}
+
 // Kernels whose dynamic LDS exceeds 64 KiB must opt in (gfx950 has 160 KiB per CU).
 template <class K>
 inline hipError_t ensure_lds(K* kernel, size_t bytes) {

@@ -152,10 +152,13 @@ __host__ __device__ constexpr int p1_waves_per_simd(int mode, int d) {
 // rows are scaled by tau once, which is exact, so the score products give tau S and
 // G = tau (UQ K^T + Q UK^T) directly (the same float32 values as scaling afterwards)
 // and each step saves the 16 multiplications of G by tau.
-// ASML (that sweep, non-causal, N a multiple of 32): the step loop runs as one
-// inline-assembly block with a fixed schedule (pass1_asm_steps) instead of the
-// compiled steps.
-template <class TT, int D, bool CAUSAL, int MODE, bool FOLD = false, bool ASML = false>
+// ASML (that sweep): steps that need no mask (whole key blocks that no query of the
+// workgroup precedes) run as one inline-assembly block with a fixed schedule
+// (pass1_asm_steps). kAsmAll: every step of the sweep needs none (non-causal, N a
+// multiple of 32), so the kernel has no compiled steps; kAsmPrefix: the compiled steps
+// take the rest (a causal sweep's diagonal blocks, a ragged last block).
+enum : int { kAsmNone = 0, kAsmAll = 1, kAsmPrefix = 2 };
+template <class TT, int D, bool CAUSAL, int MODE, bool FOLD = false, int ASML = kAsmNone>
 __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_kernel(Pass1Args a) {
   using G = Geo<TT, D>;
   using T = typename TT::elem;
@@ -165,8 +168,8 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   // and awaited one step before use; d = 128 (no register room for the deeper
   // unroll) keeps three stages, two steps ahead, compiler-visible copies.
   constexpr bool DEEP = D == 64;
-  constexpr int NT = 4, NBUF = ASML ? FB_PASS1_ASM_SLOTS : DEEP ? 4 : 3;
-  constexpr int AHEAD = ASML ? FB_PASS1_ASM_AHEAD : NBUF - 1;
+  constexpr int NT = 4, NBUF = ASML != kAsmNone ? FB_PASS1_ASM_SLOTS : DEEP ? 4 : 3;
+  constexpr int AHEAD = ASML != kAsmNone ? FB_PASS1_ASM_AHEAD : NBUF - 1;
   // The two-pass sweeps keep their four accumulator tiles in AGPRs from inline
   // assembly and are compiled with the VGPR form for everything else
   // (bob_pass1_vgpr.hip), so the element-wise work reads the score tiles where the
@@ -487,13 +490,26 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
     if constexpr (MODE == kAlphaPass) asm volatile("" : "+v"(alpha_p)::"memory");
     if constexpr (MODE == kEnergyPass) asm volatile("" : "+v"(e0_p)::"memory");
   };
-  if constexpr (ASML) {
-    static_assert(FOLD && !CAUSAL && D == 64, "scheduled loop: folded non-causal d = 64");
-    const size_t ahead = (size_t)(kt_begin + AHEAD) * kTile * D;  // copy sources of step 0
-    pass1_asm_steps(sc, gc, pc, hc, bq, buq, bdo, accA, accB, accC, accX, alpha_p, e0_p, lq, dq, src[0] + ahead,
-                    src[1] + ahead, src[2] + ahead, src[3] + ahead, lds, wave, lane, nsteps);
-  } else {
-    int j = 0;
+  int j = 0;
+  if constexpr (ASML != kAsmNone) {
+    static_assert(FOLD && D == 64 && (ASML == kAsmPrefix || !CAUSAL), "scheduled loop: folded d = 64 two-pass sweep");
+    // steps with no mask and no copy of a ragged block (kAsmAll: the caller guarantees
+    // every step qualifies)
+    const int nasm = ASML == kAsmAll ? nsteps
+                                     : pass1_asm_step_count(N, CAUSAL, qt, kt_begin, nsteps, NBUF, AHEAD);
+    if (nasm > 0) {
+      const size_t ahead = (size_t)(kt_begin + AHEAD) * kTile * D;  // copy sources of step 0
+      pass1_asm_steps(sc, gc, pc, hc, bq, buq, bdo, accA, accB, accC, accX, alpha_p, e0_p, lq, dq, src[0] + ahead,
+                      src[1] + ahead, src[2] + ahead, src[3] + ahead, lds, wave, lane, nasm, nsteps);
+      // the compiled steps take the plain dP tile (the block leaves dP - D in it)
+      if (FB_PASS1_ASM_DBIAS && nasm < nsteps) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pc[r] += dq;
+      }
+      j = nasm;
+    }
+  }
+  if constexpr (ASML != kAsmAll) {
     for (; j + NBUF <= nsteps; j += NBUF) unroll_steps(step, j, std::make_integer_sequence<int, NBUF>{});
     unroll_steps_until(step, j, nsteps, std::make_integer_sequence<int, NBUF - 1>{});
   }

@@ -36,6 +36,40 @@ FB_STUB(launch_probe_gq_atomics(float*, int, int, int, int, hipStream_t))
 }  // namespace fb
 
 static int failures = 0;
+
+// pass1_asm_step_count over every sweep of many shapes: the scheduled block computes only
+// whole key blocks that no query of its workgroup precedes, copies only whole blocks,
+// and stops at a stage boundary unless it runs the whole sweep.
+static int check_asm_step_counts() {
+  int bad = 0;
+  const int slots = 4, ahead = 3;
+  for (int N = 1; N <= 1300; N += (N < 300 ? 1 : 37)) {
+    for (int causal = 0; causal < 2; ++causal) {
+      for (int nsplit = 1; nsplit <= 9; ++nsplit) {
+        for (int qt = 0; qt < fb::row_tiles(N); ++qt) {
+          int nkt = (N + 31) / 32;
+          if (causal) nkt = nkt < (qt + 1) * 4 ? nkt : (qt + 1) * 4;
+          for (int split = 0; split < nsplit; ++split) {
+            const int kt_begin = (int)((long long)split * nkt / nsplit);
+            const int kt_end = (int)((long long)(split + 1) * nkt / nsplit);
+            const int nsteps = kt_end - kt_begin;
+            const int n = fb::pass1_asm_step_count(N, causal != 0, qt, kt_begin, nsteps, slots, ahead);
+            bool ok = n >= 0 && n <= nsteps && (n == nsteps || n % slots == 0);
+            for (int j = 0; ok && j < n; ++j) {
+              const int kt = kt_begin + j;
+              ok = (kt + 1) * 32 <= N && (!causal || kt * 32 + 31 < qt * 128);
+              if (ok && j + ahead < nsteps) ok = (kt_begin + j + ahead + 1) * 32 <= N;  // the block's copy
+            }
+            if (!ok && bad++ < 5)
+              std::printf("FAIL asm step count: N=%d causal=%d nsplit=%d qt=%d split=%d -> %d of %d\n", N, causal,
+                          nsplit, qt, split, n, nsteps);
+          }
+        }
+      }
+    }
+  }
+  return bad;
+}
 #define EXPECT(cond)                                                   \
   do {                                                                 \
     if (!(cond)) {                                                     \
@@ -52,6 +86,7 @@ static fb_status_t bob_ws(int B, int H, int N, int d, fb_dtype_t dt, float tau, 
 }
 
 int main() {
+  failures += check_asm_step_counts();
   const fb_dtype_t dts[3] = {FB_F32, FB_F16, FB_BF16};
   const int ns[] = {1, 2, 31, 32, 33, 127, 128, 129, 1000, 16384, 262144, 1 << 22, INT_MAX - 255, INT_MAX - 127,
                     INT_MAX, -1, 0, INT_MIN};

@@ -121,6 +121,27 @@ def test_generated_steps_respect_waits_and_hazards():
         assert not written & {("v", n) for n in range(243, 254)}
 
 
+def test_clobbers_cover_every_written_register():
+    """Every VGPR or AGPR the block writes (its prologue included) is either bound to an
+    output (score tiles v[0:63], row sums v254 and v255, accumulators a[0:127]) or in
+    its clobber list; no input register (v[243:253], a[128:175]) is written."""
+    g = _gen()
+    text = g.render()
+    line = next(l for l in text.splitlines() if l.startswith("#define FB_PASS1_ASM_CLOBBERS"))
+    clob = set(re.findall(r'"([va]\d+)"', line))
+    written = set()
+    for x in g.loop_text():
+        op, ops = _operands(x)
+        if (op.startswith("v_") or op.startswith("ds_read")) and ops:
+            r = _regs(ops[0])
+            if r:
+                written |= {f"{r[0]}{n}" for n in r[1]}
+    bound = {f"v{n}" for n in list(range(64)) + [254, 255]} | {f"a{n}" for n in range(128)}
+    inputs = {f"v{n}" for n in range(243, 254)} | {f"a{n}" for n in range(128, 176)}
+    assert not written & inputs
+    assert written - bound <= clob, sorted(written - bound - clob)[:5]
+
+
 SCALAR_OK = {"s_nop", "s_waitcnt", "s_mov_b32", "s_add_u32", "s_addc_u32", "s_cmp_lt_u32", "s_cmp_gt_u32",
              "s_cmp_ge_u32", "s_cbranch_scc0", "s_cbranch_scc1", "s_branch", "s_barrier"}
 
