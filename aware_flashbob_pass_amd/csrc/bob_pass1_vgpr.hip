@@ -12,7 +12,7 @@ namespace fb {
 
 template <class TT, bool CAUSAL, bool FOLD = false, int ASML = kAsmNone>
 static hipError_t launch_64(const Pass1Args& a, hipStream_t s) {
-  const size_t lds = ASML != kAsmNone ? pass1_asm_lds_bytes() : pass1_lds_bytes<TT, 64>();
+  const size_t lds = (ASML != kAsmNone ? pass1_asm_lds_bytes() : pass1_lds_bytes<TT, 64>()) + pass1_o_lds_bytes();
   hipError_t e = ensure_lds(&bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bob_pass1_kernel<TT, 64, CAUSAL, kTwoPass, FOLD, ASML>), dim3(row_tiles(a.N), a.BH, a.nsplit),

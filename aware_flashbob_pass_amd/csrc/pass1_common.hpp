@@ -30,11 +30,12 @@ struct P1 {
 
 // gQ_i and gdO_i at the 4 head dims of slots 4 r4 .. 4 r4 + 3 of the 32-wide
 // head-dim block `mbg` from their alpha-free sums, with alpha_i and e0_i already
-// summed over the lane pair of the row.
+// summed over the lane pair of the row. orow: the row of O to read (global memory,
+// or a copy in LDS), or null for the row in a.O.
 template <class TT, int D>
 __device__ inline void pass1_epilogue_quad(const f32x4& A, const f32x4& B, const f32x4& C, const f32x4& X,
                                            float alpha, float e0, int qi, int g, int bh, int mbg, int r4,
-                                           const Pass1Args& a) {
+                                           const Pass1Args& a, const typename TT::elem* orow = nullptr) {
   using T = typename TT::elem;
   const int N = a.N;
   if (qi >= N) return;
@@ -42,7 +43,7 @@ __device__ inline void pass1_epilogue_quad(const f32x4& A, const f32x4& B, const
   const int dim = mbg * 32 + kappa(r4 * 4, g);
   const float tau = a.tau;
   float o[4], q[4], x[4];
-  load4<TT>(reinterpret_cast<const T*>(a.O) + row * D + dim, o);
+  load4<TT>((orow ? orow : reinterpret_cast<const T*>(a.O) + row * D) + dim, o);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     q[e] = tau * (A[e] - alpha * B[e] - e0 * C[e]);
@@ -60,11 +61,11 @@ __device__ inline f32x4 quad_of(const f32x16& v, int r4) {
 template <class TT, int D>
 __device__ inline void pass1_epilogue_block(const f32x16& A, const f32x16& B, const f32x16& C, const f32x16& X,
                                             float alpha, float e0, int qi, int g, int bh, int mbg,
-                                            const Pass1Args& a) {
+                                            const Pass1Args& a, const typename TT::elem* orow = nullptr) {
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4)
     pass1_epilogue_quad<TT, D>(quad_of(A, r4), quad_of(B, r4), quad_of(C, r4), quad_of(X, r4), alpha, e0, qi, g,
-                               bh, mbg, r4, a);
+                               bh, mbg, r4, a, orow);
 }
 
 // alpha_i and E_i = e0_i - alpha_i D_i of the row, and for pass 2 L_i log2(e) and
@@ -80,6 +81,18 @@ __device__ inline void pass1_write_scalars(float alpha, float e0, int qi, int g,
   a.c[row] = fmaf(alpha, dq, E);
 }
 
+// The same with L_i log2(e) and D_i of the row already in registers.
+__device__ inline void pass1_write_scalars(float alpha, float e0, int qi, int g, int bh, const Pass1Args& a, float l2,
+                                           float dq) {
+  if (qi >= a.N || g != 0) return;
+  const size_t row = (size_t)bh * a.N + qi;
+  const float E = e0 - alpha * dq;
+  a.alpha[row] = alpha;
+  a.E[row] = E;
+  a.l2[row] = l2;
+  a.c[row] = fmaf(alpha, dq, E);
+}
+
 // gQ_i, gdO_i, alpha_i, E_i from the alpha-free sums of one wave.
 template <class TT, int D>
 __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
@@ -92,6 +105,22 @@ __device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f
   for (int mbl = 0; mbl < MBA; ++mbl)
     pass1_epilogue_block<TT, D>(A[mbl], B[mbl], C[mbl], X[mbl], alpha, e0, qi, g, bh, mbl, a);
   pass1_write_scalars(alpha, e0, qi, g, bh, a);
+}
+
+// The same with the row of O read from `orow` (a copy in LDS) and L_i log2(e), D_i
+// from registers: no global load at the end of the sweep.
+template <class TT, int D>
+__device__ inline void pass1_epilogue(const f32x16 (&A)[P1<TT, D>::MBA], const f32x16 (&B)[P1<TT, D>::MBA],
+                                      const f32x16 (&C)[P1<TT, D>::MBA], const f32x16 (&X)[P1<TT, D>::MBA],
+                                      float alpha_p, float e0_p, int qi, int g, int bh, const Pass1Args& a,
+                                      const typename TT::elem* orow, float l2, float dq) {
+  constexpr int MBA = P1<TT, D>::MBA;
+  const float alpha = pair_sum32(alpha_p);
+  const float e0 = pair_sum32(e0_p);
+#pragma unroll
+  for (int mbl = 0; mbl < MBA; ++mbl)
+    pass1_epilogue_block<TT, D>(A[mbl], B[mbl], C[mbl], X[mbl], alpha, e0, qi, g, bh, mbl, a, orow);
+  pass1_write_scalars(alpha, e0, qi, g, bh, a, l2, dq);
 }
 
 // Raw accumulators and row partials of one wave for split `split`.

@@ -201,6 +201,41 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   const int q0 = qt * kBlockRows + wave * kTile;
   const int qi = q0 + n;
 
+  int nkt = (N + kTile - 1) / kTile;
+  if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
+  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
+  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
+  const int nsteps = kt_end - kt_begin;
+
+  auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
+  auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
+
+  // tiles a mode reads: K always, V for dP, UK for G, UV for H
+  constexpr bool NEED_TILE[NT] = {true, NEED_DP, NEED_G, NEED_H};
+  auto issue = [&](int stg, int j) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (NEED_TILE[t])
+        stage_direct<TT, D, kBlock / 64, DEEP>(src[t], (kt_begin + j) * kTile, N,
+                                                lds + (stg * NT + t) * G::ROW_ELEMS, wave, lane);
+  };
+  // Copies first, then the resident rows, so that their latencies overlap: the
+  // compiler's own waits for those loads only get stricter with older copies in flight.
+  // Without splits the epilogue needs the wave's rows of O (gdO = X - alpha O): they
+  // are copied into LDS beside the stages, so the end of the sweep reads no global memory.
+  T* o_lds = lds + NBUF * NT * G::ROW_ELEMS + wave * kTile * D;
+  if constexpr (TWO && D == 64) {
+    if (a.nsplit == 1) {
+      const T* osrc = reinterpret_cast<const T*>(a.O) + base;
+#pragma unroll
+      for (int c = 0; c < kTile * D / (64 * 8); ++c) {  // 64 lanes x 16 bytes a copy
+        const int slot = c * 64 + lane, row = slot / (D / 8), ch = slot % (D / 8);
+        glds16<DEEP>(osrc + (size_t)min(q0 + row, N - 1) * D + ch * 8, o_lds + c * 64 * 8);
+      }
+    }
+  }
+  for (int j = 0; j < AHEAD && j < nsteps; ++j) issue(j, j);
+
   V bq[DK], bdo[DK], buq[DK];
   load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
   load_resident<TT, D>(reinterpret_cast<const T*>(a.dO) + base, qi, N, g, bdo);
@@ -233,24 +268,6 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   }
   float alpha_p = 0.f, e0_p = 0.f;
 
-  int nkt = (N + kTile - 1) / kTile;
-  if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
-  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
-  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
-  const int nsteps = kt_end - kt_begin;
-
-  auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
-  auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
-
-  // tiles a mode reads: K always, V for dP, UK for G, UV for H
-  constexpr bool NEED_TILE[NT] = {true, NEED_DP, NEED_G, NEED_H};
-  auto issue = [&](int stg, int j) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (NEED_TILE[t])
-        stage_direct<TT, D, kBlock / 64, DEEP>(src[t], (kt_begin + j) * kTile, N,
-                                                lds + (stg * NT + t) * G::ROW_ELEMS, wave, lane);
-  };
   // The stage copies are invisible to the compiler (inline assembly), so make it
   // complete its own loads of the resident rows and row scalars here: otherwise it
   // could wait for them inside the loop with a vmcnt(0) that also drains the copies.
@@ -258,7 +275,6 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
     settle_regs(bq, bdo, lq, dq, al, er);
     if constexpr (NEED_G) settle_regs(buq);
   }
-  for (int j = 0; j < AHEAD && j < nsteps; ++j) issue(j, j);
   wait_vmem();
   __syncthreads();
 
@@ -517,7 +533,9 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
   if constexpr (TWO) {
     if constexpr (ASM_ACC) pass1_acc_settle<MBA>(accA, accB, accC, accX);
     if (a.nsplit == 1) {
-      pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
+      if constexpr (D == 64) pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a, o_lds + n * D,
+                                                    lq, dq);
+      else pass1_epilogue<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, qi, g, bh, a);
       return;
     }
     pass1_write_record<TT, D>(accA, accB, accC, accX, alpha_p, e0_p, split, bh, qt, wave, lane, a);
@@ -533,6 +551,8 @@ __global__ __launch_bounds__(kBlock, p1_waves_per_simd(MODE, D)) void bob_pass1_
 
 // LDS of the scheduled loop: FB_PASS1_ASM_SLOTS stages of K, V, UK, UV.
 inline size_t pass1_asm_lds_bytes() { return (size_t)FB_PASS1_ASM_SLOTS * 4 * 32 * 64 * 2; }
+// LDS after the stages of the two-pass d = 64 kernel: each wave's rows of O (16-bit).
+inline size_t pass1_o_lds_bytes() { return (size_t)4 * 32 * 64 * 2; }
 
 template <class TT, int D>
 inline size_t pass1_lds_bytes() {
