@@ -46,7 +46,7 @@ KERNELS_PER_CALL = {
 TRACE_KERNELS = {
     "attn_fwd_stats": "attn_fwd_kernel<fb::BF16, 64, false, true>",
     "attn_fwd_combine": "attn_fwd_combine_kernel<fb::BF16, 64, true>",
-    "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0, true, true>",
+    "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0, true, 1>",
     "bob_pass1_combine": "bob_pass1_combine_kernel<fb::BF16, 64>",
     "bob_pass2": "bob_pass2_kernel<fb::BF16, 64, false, false>",
     "bob_pass2_reduce": "bob_pass2_reduce_kernel<fb::BF16, 64>",
