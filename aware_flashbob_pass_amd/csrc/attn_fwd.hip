@@ -11,7 +11,15 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#ifndef FB_FWD_SKEW
+#define FB_FWD_SKEW 1
+#endif
+
 namespace fb {
+
+// Stage ring of the skewed statistics sweep: slots and copy distance in steps.
+constexpr int kFwdSkewSlots = 6;
+constexpr int kFwdSkewAhead = 5;
 
 // O, L and (optionally) D of one wave from its unnormalised O^T accumulators,
 // running max m (log2 units, equal in lanes n and n + 32) and per-lane partial
@@ -69,6 +77,25 @@ __device__ inline void fwd_epilogue(const f32x16 (&acc)[Geo<TT, D>::MB], float m
 // lane's sum, so the limit bounds the weight operands: bf16 has the float32
 // exponent range and takes 2^32; fp16 operands must stay below 65504, its
 // largest finite value, and take 2^15. After a redo every weight is at most 1.
+// The end of a statistics sweep: O, L (and D) of the wave's rows when the keys are not
+// split, else the wave's split record (accumulators, m, l) for the merge.
+template <class TT, int D, bool WITH_D>
+__device__ inline void fwd_finish(const f32x16 (&acc)[Geo<TT, D>::MB], float m, float l, int qt, int bh, int split,
+                                  int wave, int lane, const FwdArgs& a) {
+  constexpr int MB = Geo<TT, D>::MB;
+  const int N = a.N;
+  if (a.nsplit == 1) {
+    fwd_epilogue<TT, D, WITH_D>(acc, m, l, qt * kBlockRows + wave * kTile + (lane & 31), lane >> 5, bh, a);
+    return;
+  }
+  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + qt) * 4 + wave;
+  float* R = a.part + rec * fwd_record_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) store_tile16(R + mb * 1024, lane, acc[mb]);  // [MB] quad-major tiles
+  R[MB * 16 * 64 + lane] = m;
+  R[MB * 16 * 64 + 64 + lane] = l;
+}
+
 template <class TT>
 __device__ constexpr float lazy_limit() {
   return std::is_same_v<TT, F16> ? 32768.f : 4294967296.f;  // 2^15 : 2^32
@@ -200,16 +227,156 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
   if (j < nsteps) step(I0{}, j);
   if (j + 1 < nsteps) step(I1{}, j + 1);
 
-  if (a.nsplit == 1) {
-    fwd_epilogue<TT, D, WITH_D>(acc, m, l, qi, g, bh, a);
-    return;
-  }
-  const size_t rec = (((size_t)split * a.BH + bh) * row_tiles(N) + qt) * 4 + wave;
-  float* R = a.part + rec * fwd_record_floats(D);
+  fwd_finish<TT, D, WITH_D>(acc, m, l, qt, bh, split, wave, lane, a);
+}
+
+// Two-step skew of the same sweep. Step j issues the score products of step j + 2
+// and the P V products of step j, and forms the weights of step j + 1 from the score
+// tile step j - 1 issued: no part of a step waits for another part of it, so the
+// compiler can place the exponentials among the products. Score tiles and weights
+// are double-buffered. The stage ring has NBUF slots and the copies, issued from
+// inline assembly, run AHEAD stages ahead; step j reads K of stage j + 2 and V of
+// stage j, and its end waits only for stage j + 3.
+// The weights take one form, p = 2^(fma(s, tau log2 e, -m)), on every step; a step
+// whose keys need a mask (the ragged last block, the causal diagonal) or whose
+// weights reach the lazy limit forms them again on a slow path, which applies the
+// mask and, for the limit, moves m to the row maximum as attn_fwd_kernel does. A
+// redo of step j + 1's weights rescales the accumulators after step j's products,
+// which were formed with the same reference as the sums.
+template <class TT, int D, bool CAUSAL, bool WITH_D>
+__global__ __launch_bounds__(kBlock, 2) void attn_fwd_skew_kernel(FwdArgs a) {
+  using G = Geo<TT, D>;
+  using T = typename TT::elem;
+  using V = typename TT::vec;
+  constexpr int MB = G::MB, DK = G::DK, NK = G::NK;
+  constexpr int NT = 2, NBUF = kFwdSkewSlots, AHEAD = kFwdSkewAhead;
+  constexpr int COPIES = NT * stage_copies<D, kBlock / 64>();  // per wave and stage
+  static_assert(TT::KPL == 8 && NK == 2, "16-bit inputs only");
+  static_assert(NBUF % 2 == 0 && AHEAD >= 3 && AHEAD < NBUF, "stage ring");
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int g = lane >> 5, n = lane & 31;
+  int qt, bh;
+  tile_and_head<CAUSAL, true>(qt, bh);
+  const int N = a.N, split = blockIdx.z;
+  const size_t base = (size_t)bh * N * D;
+  const T* src[NT] = {reinterpret_cast<const T*>(a.K) + base, reinterpret_cast<const T*>(a.V) + base};
+  const int q0 = qt * kBlockRows + wave * kTile;
+  const int qi = q0 + n;
+
+  int nkt = (N + kTile - 1) / kTile;
+  if (CAUSAL) nkt = min(nkt, (qt + 1) * (kBlockRows / kTile));
+  const int kt_begin = (int)((long long)split * nkt / a.nsplit);
+  const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
+  const int nsteps = kt_end - kt_begin;
+  auto stage = [&](int slot, int t) __attribute__((always_inline)) { return lds + (slot * NT + t) * G::ROW_ELEMS; };
+  auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
+  auto issue = [&](int slot, int j) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) store_tile16(R + mb * 1024, lane, acc[mb]);  // [MB] quad-major tiles
-  R[MB * 16 * 64 + lane] = m;
-  R[MB * 16 * 64 + 64 + lane] = l;
+    for (int t = 0; t < NT; ++t)
+      stage_direct<TT, D, kBlock / 64, true>(src[t], (kt_begin + j) * kTile, N, stage(slot, t), wave, lane);
+  };
+
+  V bq[DK];
+  load_resident<TT, D>(reinterpret_cast<const T*>(a.Q) + base, qi, N, g, bq);
+  settle_regs(bq);
+  for (int j = 0; j < AHEAD && j < nsteps; ++j) issue(j, j);
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+  float m = -1e30f, l = 0.f;
+  const float cs = a.tau * kLog2e;
+  wait_vmem();
+  __syncthreads();
+
+  f32x16 sb[2];
+  V pp[2][NK];
+  auto scores = [&](f32x16& s, int slot) __attribute__((always_inline)) {
+    s = zero16();
+#pragma unroll
+    for (int t = 0; t < DK; ++t) s = TT::mfma(lds_row_op<TT, D>(stage(slot, 0), n, t, g), bq[t], s);
+  };
+  // Weights of step j from its score tile, with their sum added to l.
+  auto weights = [&](const f32x16& sc, V (&p)[NK], int j) __attribute__((always_inline)) {
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(fmaf(sc[r], cs, -m));
+      ls += pr;
+      vset<TT>(p[r >> 3], r & 7, pr);
+    }
+    const int k0 = (kt_begin + j) * kTile;
+    const bool masked = k0 + kTile > N || (CAUSAL && k0 + kTile - 1 > q0);  // wave-uniform
+    if (masked || __ballot(lazy_redo(ls, lazy_limit<TT>()))) {
+      bool keep[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kappa(r, g);
+        keep[r] = !masked || (key < N && (!CAUSAL || key <= qi));
+      }
+      auto form = [&]() __attribute__((always_inline)) {
+        ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = keep[r] ? fast_exp2(fmaf(sc[r], cs, -m)) : 0.f;
+          ls += pr;
+          vset<TT>(p[r >> 3], r & 7, pr);
+        }
+      };
+      if (masked) form();
+      if (__ballot(lazy_redo(ls, lazy_limit<TT>()))) {  // move m to the row maximum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (keep[r]) mx = fmaxf(mx, sc[r] * cs);
+        mx = pair_max32(mx);
+        const float mnew = fmaxf(m, mx);
+        const float f = fast_exp2(m - mnew);
+        l *= f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] *= f;
+        m = mnew;
+        form();
+      }
+    }
+    l += ls;
+  };
+
+  if (nsteps > 0 && active(0)) scores(sb[0], 0);
+  if (nsteps > 1 && active(1)) scores(sb[1], 1);
+  if (nsteps > 0 && active(0)) weights(sb[0], pp[0], 0);
+
+  // FULL: steps j + 1 .. j + AHEAD exist (no tail checks)
+  auto step = [&](auto I_c, int j, auto full_c) __attribute__((always_inline)) {
+    constexpr int I = decltype(I_c)::value;
+    constexpr bool FULL = decltype(full_c)::value;
+    constexpr int SJ = I % NBUF, SJ2 = (I + 2) % NBUF, SJA = (I + AHEAD) % NBUF;
+    const bool copy = FULL || j + AHEAD < nsteps;
+    if (copy) issue(SJA, j + AHEAD);  // slot SJA was last read in step j + AHEAD - NBUF < j
+    if ((FULL || j + 2 < nsteps) && active(j + 2)) scores(sb[I % 2], SJ2);
+    if (active(j)) {
+#pragma unroll
+      for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = TT::mfma(lds_tr_op<TT, D>(stage(SJ, 1), mb, t, lane), pp[I % 2][t], acc[mb]);
+    }
+    if ((FULL || j + 1 < nsteps) && active(j + 1)) weights(sb[(I + 1) % 2], pp[(I + 1) % 2], j + 1);
+    if (copy) wait_vmem_keep<(AHEAD - 3) * COPIES>();  // stage j + 3 has landed
+    else wait_vmem();
+    __syncthreads();
+  };
+  using Full = std::true_type;
+  using Tail = std::false_type;
+  auto full = [&](auto I_c, int j) __attribute__((always_inline)) { step(I_c, j, Full{}); };
+  auto tail = [&](auto I_c, int j) __attribute__((always_inline)) { step(I_c, j, Tail{}); };
+  int j = 0;
+  for (; j + NBUF + AHEAD <= nsteps; j += NBUF) unroll_steps(full, j, std::make_integer_sequence<int, NBUF>{});
+  unroll_steps_until(tail, j, nsteps, std::make_integer_sequence<int, NBUF + AHEAD>{});
+
+  fwd_finish<TT, D, WITH_D>(acc, m, l, qt, bh, split, wave, lane, a);
 }
 
 // Merge the split records of one wave (fixed split order) and apply the epilogue.
@@ -388,11 +555,21 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int BH, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_simple_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH), dim3(kBlock), lds,
                        s, a);
   } else {
-    const size_t lds = (size_t)3 * 2 * G::ROW_ELEMS * sizeof(typename TT::elem);
-    hipError_t e = ensure_lds(&attn_fwd_kernel<TT, D, CAUSAL, WITH_D>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_fwd_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH, a.nsplit), dim3(kBlock),
-                       lds, s, a);
+    // The skew pays off on long non-causal sweeps at d = 64: at d = 128 it needs more than
+    // 256 registers, and causal sweeps are too short for its longer prologue and tail.
+    if constexpr (FB_FWD_SKEW && D == 64 && !CAUSAL) {
+      const size_t lds = (size_t)kFwdSkewSlots * 2 * G::ROW_ELEMS * sizeof(typename TT::elem);
+      hipError_t e = ensure_lds(&attn_fwd_skew_kernel<TT, D, CAUSAL, WITH_D>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_fwd_skew_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH, a.nsplit),
+                         dim3(kBlock), lds, s, a);
+    } else {
+      const size_t lds = (size_t)3 * 2 * G::ROW_ELEMS * sizeof(typename TT::elem);
+      hipError_t e = ensure_lds(&attn_fwd_kernel<TT, D, CAUSAL, WITH_D>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_fwd_kernel<TT, D, CAUSAL, WITH_D>), dim3(row_tiles(a.N), BH, a.nsplit),
+                         dim3(kBlock), lds, s, a);
+    }
   }
   return hipGetLastError();
 }

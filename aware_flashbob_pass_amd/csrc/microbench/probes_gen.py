@@ -26,6 +26,17 @@ Probes (each prints one line "name: value unit"):
   element pairs beside the score products.
 - gchain_*: 20 score products per step with the G tile as one chain of dependent
   products two issue slots apart, or split over two tiles.
+- rate_*: 64 independent vector instructions of one kind per step (v_fma_f32,
+  v_exp_f32), one wave per SIMD: cycles per instruction.
+- fwddep_*: one step of the statistics kernel (32 queries x 32 keys per wave, d = 64:
+  4 score products chained over the head dimension, 4 P V products into two
+  accumulator tiles, 16 weights p = 2^(fma(s, c, -m)) with their sum and 8 bf16 packs,
+  4 ds_read_b128 + 8 ds_read_b64_tr_b16, one barrier) at one wave per SIMD, in two
+  orders: "phased" (this step's score products, then its weights, then its P V
+  products: the order of the compiled kernel) and "skewed" (the score products of step
+  j + 2 and the P V products of step j beside the weights of step j + 1, so nothing in a
+  step waits for anything else in it); "skewed_noexp" replaces the exponentials by
+  moves, "skewed_mfma" keeps only the products and "skewed_valu" only the vector work.
 """
 
 import os
@@ -291,10 +302,139 @@ def gchain(split):
     return ins, []
 
 
+def rate(kind):
+    ins = []
+    for k in range(64):
+        r = 100 + (k % 64)
+        ins.append(f"v_exp_f32 v{r}, v{r}" if kind == "exp" else f"v_fma_f32 v{r}, v{r}, v{r + 64}, v{r + 65}")
+    return ins, []
+
+
+def fwd_dep(order):
+    """One statistics-kernel step per list entry pair (two steps per body, buffers swapped).
+    Registers: score tiles v[0:15] / v[16:31]; weights (packed) v[64:71] / v[72:79]; Q
+    operands v[80:95]; K row operands v[96:111] / v[212:227]; V^T operands v[112:127] /
+    v[228:243]; element temporaries v[128:159]; step sum v200, row sum v201, -m v202,
+    scale v247; accumulators a[0:31]."""
+    use_m = order != "skewed_valu"
+    use_v = order != "skewed_mfma"
+
+    def elem_pair(sbuf, pbuf, p):
+        a, b = 2 * p, 2 * p + 1
+        ta, tb = 128 + a, 128 + b
+        ex = "v_mov_b32" if order == "skewed_noexp" else "v_exp_f32"
+        out = [f"v_fma_f32 v{ta}, v{sbuf + a}, v247, v202", f"v_fma_f32 v{tb}, v{sbuf + b}, v247, v202",
+               f"{ex} v{ta}, v{ta}", f"{ex} v{tb}, v{tb}",
+               (f"v_add_f32 v200, v{ta}, v{tb}" if p == 0 else f"v_add_f32 v200, v200, v{ta}"),
+               f"v_cvt_pk_bf16_f32 v{pbuf + p}, v{ta}, v{tb}"]
+        if p > 0:
+            out.insert(5, f"v_add_f32 v200, v200, v{tb}")
+        return out
+
+    def step(s_next, s_cur, p_cur, p_prev, ob):
+        """s_next: tile the score products write; s_cur: tile the weights read; p_cur: weights
+        written; p_prev: weights the P V products read; ob: operand buffer (0/1)."""
+        krow, vtr = (96, 112) if ob == 0 else (212, 228)
+        nk, nv = (212, 228) if ob == 0 else (96, 112)
+        score = [f"v_mfma_f32_32x32x16_bf16 v[{s_next}:{s_next + 15}], v[{krow + 4 * t}:{krow + 4 * t + 3}], "
+                 f"v[{80 + 4 * t}:{80 + 4 * t + 3}], " + ("0" if t == 0 else f"v[{s_next}:{s_next + 15}]")
+                 for t in range(4)]
+        pv = [f"v_mfma_f32_32x32x16_bf16 a[{16 * (i % 2)}:{16 * (i % 2) + 15}], v[{vtr + 4 * i}:{vtr + 4 * i + 3}], "
+              f"v[{p_prev + 4 * (i // 2)}:{p_prev + 4 * (i // 2) + 3}], a[{16 * (i % 2)}:{16 * (i % 2) + 15}]"
+              for i in range(4)]
+        valu = [x for p in range(8) for x in elem_pair(s_cur, p_cur, p)]
+        valu += ["v_add_f32 v201, v201, v200", "v_cmp_ge_u32 vcc, v200, v247"]
+        reads = [f"ds_read_b128 v[{nk + 4 * t}:{nk + 4 * t + 3}], v244 offset:{t * 1024}" for t in range(4)]
+        reads += [f"ds_read_b64_tr_b16 v[{nv + 2 * i}:{nv + 2 * i + 1}], v246 offset:{4096 + i * 512}"
+                  for i in range(8)]
+        if not use_m:
+            score, pv = [], []
+        if not use_v:
+            valu = []
+        ins = []
+        if order == "phased":
+            # this step's tile: score products, then (after the chain completes) the weights,
+            # then the P V products; the operand reads of the next step go out with the products
+            ins += score
+            ins += reads[:4]
+            ins += valu
+            ins += ["s_nop 1"]
+            ins += pv
+            ins += reads[4:]
+        else:
+            mf = [x for pair in zip(score, pv) for x in pair] if use_m else []
+            per = -(-len(valu) // max(1, len(mf))) if mf else len(valu)
+            rd = list(reads)
+            for k in range(max(len(mf), 1)):
+                if k < len(mf):
+                    ins.append(mf[k])
+                ins += valu[:per]
+                valu = valu[per:]
+                if k >= 1:
+                    ins += rd[:2]
+                    rd = rd[2:]
+            ins += valu + rd
+        ins += ["s_waitcnt lgkmcnt(0)", "s_barrier"]
+        return ins
+
+    if order == "phased":
+        a = step(0, 0, 64, 64, 0)
+        b = step(16, 16, 72, 72, 1)
+    else:
+        # step j: products write tile (j+2)%2, weights read tile (j+1)%2 and write pack (j+1)%2,
+        # P V reads pack j%2
+        a = step(0, 16, 72, 64, 0)
+        b = step(16, 0, 64, 72, 1)
+    return _mfma_read_waits(a + b), []
+
+
+def _regs(op):
+    """VGPR numbers an operand names (v5, v[0:15]); none for AGPRs, constants, vcc."""
+    import re
+    m = re.fullmatch(r"v(\d+)", op) or re.fullmatch(r"v\[(\d+):(\d+)\]", op)
+    if not m:
+        return set()
+    lo = int(m.group(1))
+    hi = int(m.group(2)) if m.lastindex == 2 else lo
+    return set(range(lo, hi + 1))
+
+
+def _mfma_read_waits(ins, need=19):
+    """Insert s_nop before any vector instruction that reads a VGPR an MFMA wrote fewer than
+    `need` wait states earlier (the loop body repeats, so the scan runs over it twice)."""
+    def ops(x):
+        parts = x.replace(",", " ").split()
+        return parts[0], parts[1:]
+
+    out, last = [], {}
+    for rep in range(2):
+        pos = 0
+        res = []
+        for x in ins:
+            op, args = ops(x)
+            if op.startswith("v_") and not op.startswith("v_mfma") and args:
+                reads = set().union(*[_regs(a) for a in args[1:]]) if len(args) > 1 else set()
+                gap = min([pos - last[r] for r in reads if r in last] or [need])
+                if gap < need:
+                    res.append(f"s_nop {need - gap - 1}")
+                    pos += need - gap
+            if op.startswith("v_mfma") and args[0].startswith("v"):
+                for r in _regs(args[0]):
+                    last[r] = pos
+            pos += int(op == "s_nop" and args[0]) + 1 if op == "s_nop" else 1
+            res.append(x)
+        out = res
+        last = {r: v - pos for r, v in last.items()}
+    return out
+
+
 SKELETONS = ([(f"p1mix_{m}", p1_mix(m), 1) for m in ("mfma", "valu", "lds", "mfma_valu", "mfma_lds", "full")] +
              [(f"p1dep_{o}", p1_dep(o), 2) for o in ("interleaved", "phased")] +
              [(f"p2dep_split{s}", p2_dep(s), 2) for s in (0, 2, 4)] +
-             [(f"gchain_{n}", gchain(s), 1) for n, s in (("one_chain", False), ("split", True))])
+             [(f"gchain_{n}", gchain(s), 1) for n, s in (("one_chain", False), ("split", True))] +
+             [(f"rate_{k}", rate(k), 64) for k in ("fma", "exp")] +
+             [(f"fwddep_{o}", fwd_dep(o), 2) for o in ("phased", "skewed", "skewed_noexp", "skewed_mfma",
+                                                          "skewed_valu")])
 
 
 def _skeleton_kernel(name, ins, addr_regs):

@@ -44,7 +44,7 @@ KERNELS_PER_CALL = {
 }
 # the device kernel (rocprofv3 name prefix) behind each library name at long_16k (bf16, d = 64, non-causal)
 TRACE_KERNELS = {
-    "attn_fwd_stats": "attn_fwd_kernel<fb::BF16, 64, false, true>",
+    "attn_fwd_stats": "attn_fwd_skew_kernel<fb::BF16, 64, false, true>",
     "attn_fwd_combine": "attn_fwd_combine_kernel<fb::BF16, 64, true>",
     "bob_pass1": "bob_pass1_kernel<fb::BF16, 64, false, 0, true, 1>",
     "bob_pass1_combine": "bob_pass1_combine_kernel<fb::BF16, 64>",
@@ -215,7 +215,8 @@ def _makespan(jobs, slots):
 
 # kernel families of a BoB call (16-bit): name prefix, how its grid walks the sequence,
 # and workgroups one compute unit holds (d = 64; d = 128 holds one of each)
-SHAPE_KERNELS = (("statistics", "attn_fwd_kernel<", "rows", 2),
+SHAPE_KERNELS = (("statistics", "attn_fwd_skew_kernel<", "rows", 2),
+                 ("statistics", "attn_fwd_kernel<", "rows", 2),
                  ("pass 1", "bob_pass1_kernel<", "rows", 1),
                  ("pass 1", "bob_pass1_q16_kernel<", "rows", 1),
                  ("pass 2", "bob_pass2_kernel<", "cols", 2))
@@ -548,7 +549,8 @@ def digest_reduction(out, copy_fetch, copy_write, *runs):
 
 SQ_COMMAND = ("rocprofv3 --pmc {counters} -d <{tag}> -o run --output-format csv -- python3 bench.py --steps 5 "
               "--warmup 2 --no-cpu --no-endpoint --no-parity --settle-s 0")
-KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
+KERNEL_UNITS = {"attn_fwd_kernel<": UNITS["stats"], "attn_fwd_skew_kernel<": UNITS["stats"],
+                "bob_pass1_kernel<": UNITS["pass1"], "bob_pass2_kernel<": UNITS["pass2"]}
 
 
 def digest_sq(out, trace_dir, *runs):
