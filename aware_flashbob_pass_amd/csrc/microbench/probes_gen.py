@@ -28,6 +28,9 @@ Probes (each prints one line "name: value unit"):
   products two issue slots apart, or split over two tiles.
 - rate_*: 64 independent vector instructions of one kind per step (v_fma_f32,
   v_exp_f32), one wave per SIMD: cycles per instruction.
+- rate_fma_banks, rate_add_chain, rate_exp_dep: the same with the FMA's three sources
+  in three register banks, a chain of dependent adds, and exponential/add pairs whose add
+  reads the exponential.
 - fwddep_*: one step of the statistics kernel (32 queries x 32 keys per wave, d = 64:
   4 score products chained over the head dimension, 4 P V products into two
   accumulator tiles, 16 weights p = 2^(fma(s, c, -m)) with their sum and 8 bf16 packs,
@@ -36,7 +39,9 @@ Probes (each prints one line "name: value unit"):
   products: the order of the compiled kernel) and "skewed" (the score products of step
   j + 2 and the P V products of step j beside the weights of step j + 1, so nothing in a
   step waits for anything else in it); "skewed_noexp" replaces the exponentials by
-  moves, "skewed_mfma" keeps only the products and "skewed_valu" only the vector work.
+  moves, "skewed_mfma" keeps only the products and "skewed_valu" only the vector work;
+  "skewed_banks" is "skewed" with no two VGPR sources of an instruction in one register
+  bank and the step's sum split over two partial sums.
 """
 
 import os
@@ -306,7 +311,16 @@ def rate(kind):
     ins = []
     for k in range(64):
         r = 100 + (k % 64)
-        ins.append(f"v_exp_f32 v{r}, v{r}" if kind == "exp" else f"v_fma_f32 v{r}, v{r}, v{r + 64}, v{r + 65}")
+        if kind == "exp":
+            ins.append(f"v_exp_f32 v{r}, v{r}")
+        elif kind == "fma_banks":  # sources in three different banks
+            ins.append(f"v_fma_f32 v{r}, v{r}, v{r + 65}, v{r + 66}")
+        elif kind == "add_chain":  # every add reads the previous one's result
+            ins.append(f"v_add_f32 v99, v99, v{r}")
+        elif kind == "exp_dep":  # exponential, then an add that reads it
+            ins.append(f"v_exp_f32 v{r}, v{r}" if k % 2 == 0 else f"v_add_f32 v{r}, v{r - 1}, v{r + 64}")
+        else:
+            ins.append(f"v_fma_f32 v{r}, v{r}, v{r + 64}, v{r + 65}")
     return ins, []
 
 
@@ -323,6 +337,17 @@ def fwd_dep(order):
         a, b = 2 * p, 2 * p + 1
         ta, tb = 128 + a, 128 + b
         ex = "v_mov_b32" if order == "skewed_noexp" else "v_exp_f32"
+        if order == "skewed_banks":
+            # no two VGPR sources of one instruction in the same bank (bank = register
+            # number mod 4): the scale as an inline constant, -m in v202 (bank 2) for
+            # elements in banks 0/1 and in v205 (bank 1) for banks 2/3, and two partial
+            # sums, v203 (bank 3) for the even elements and v206 (bank 2) for the odd ones
+            nm = "v202" if a % 4 < 2 else "v205"
+            out = [f"v_fma_f32 v{ta}, v{sbuf + a}, 0.5, {nm}", f"v_fma_f32 v{tb}, v{sbuf + b}, 0.5, {nm}",
+                   f"{ex} v{ta}, v{ta}", f"{ex} v{tb}, v{tb}",
+                   f"v_add_f32 v203, v203, v{ta}", f"v_add_f32 v206, v206, v{tb}",
+                   f"v_cvt_pk_bf16_f32 v{pbuf + p}, v{ta}, v{tb}"]
+            return out
         out = [f"v_fma_f32 v{ta}, v{sbuf + a}, v247, v202", f"v_fma_f32 v{tb}, v{sbuf + b}, v247, v202",
                f"{ex} v{ta}, v{ta}", f"{ex} v{tb}, v{tb}",
                (f"v_add_f32 v200, v{ta}, v{tb}" if p == 0 else f"v_add_f32 v200, v200, v{ta}"),
@@ -343,7 +368,10 @@ def fwd_dep(order):
               f"v[{p_prev + 4 * (i // 2)}:{p_prev + 4 * (i // 2) + 3}], a[{16 * (i % 2)}:{16 * (i % 2) + 15}]"
               for i in range(4)]
         valu = [x for p in range(8) for x in elem_pair(s_cur, p_cur, p)]
-        valu += ["v_add_f32 v201, v201, v200", "v_cmp_ge_u32 vcc, v200, v247"]
+        if order == "skewed_banks":
+            valu += ["v_add_f32 v200, v203, v206", "v_add_f32 v201, v201, v200", "v_cmp_ge_u32 vcc, v200, v247"]
+        else:
+            valu += ["v_add_f32 v201, v201, v200", "v_cmp_ge_u32 vcc, v200, v247"]
         reads = [f"ds_read_b128 v[{nk + 4 * t}:{nk + 4 * t + 3}], v244 offset:{t * 1024}" for t in range(4)]
         reads += [f"ds_read_b64_tr_b16 v[{nv + 2 * i}:{nv + 2 * i + 1}], v246 offset:{4096 + i * 512}"
                   for i in range(8)]
@@ -434,7 +462,8 @@ SKELETONS = ([(f"p1mix_{m}", p1_mix(m), 1) for m in ("mfma", "valu", "lds", "mfm
              [(f"gchain_{n}", gchain(s), 1) for n, s in (("one_chain", False), ("split", True))] +
              [(f"rate_{k}", rate(k), 64) for k in ("fma", "exp")] +
              [(f"fwddep_{o}", fwd_dep(o), 2) for o in ("phased", "skewed", "skewed_noexp", "skewed_mfma",
-                                                          "skewed_valu")])
+                                                          "skewed_valu", "skewed_banks")] +
+             [(f"rate_{k}", rate(k), 64) for k in ("fma_banks", "add_chain", "exp_dep")])
 
 
 def _skeleton_kernel(name, ins, addr_regs):
