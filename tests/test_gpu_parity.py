@@ -243,6 +243,34 @@ def test_attn_fwd_stats(dtype, d, causal):
     assert rel(dvec.cpu().double().numpy(), d_ref) <= tol
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("ragged", [False, True])
+@pytest.mark.parametrize("steps", [1, 2, 5, 6, 7, 10, 11, 12, 16, 17, 22])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_attn_fwd_stats_step_counts(dtype, steps, ragged, splits):
+    """Non-causal d = 64 statistics sweeps of 1 .. 22 steps of 32 keys (the skewed
+    kernel: sweeps shorter than 11 steps run only its tail steps, longer ones one or two
+    six-step groups and then every tail length), whole or with a ragged last block, in
+    one sweep per row tile or split in two (sweeps that start at a nonzero key block)."""
+    fb = _fb()
+    N = 32 * steps - (13 if ragged else 0)
+    w = workload.custom(1, 2, N, 64, dtype, False)
+    cpu, g = _gpu_inputs(w, 21)
+    _note(f"case stats steps={steps} N={N} {dtype} splits={splits}")
+    fb.set_tuning(splits, 0)
+    try:
+        o, lse, dvec = fb.attn_fwd(g["Q"], g["K"], g["V"], tau=w.scale, causal=False, do=g["dO"])
+        torch.cuda.synchronize()
+    finally:
+        fb.set_tuning(0, 0)
+    o_ref, l_ref = oracle.attention_forward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), w.scale, False)
+    _, _, _, d_ref = oracle.first_backward(to_f64(cpu["Q"]), to_f64(cpu["K"]), to_f64(cpu["V"]), to_f64(cpu["dO"]),
+                                           w.scale, False)
+    assert rel(to_f64(o.cpu()), o_ref) <= TOL[dtype]
+    assert rel(lse.cpu().double().numpy(), l_ref) <= 1e-3
+    assert rel(dvec.cpu().double().numpy(), d_ref) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
