@@ -65,7 +65,8 @@ class Ins:
     def __init__(self, text, asm):
         parts = text.split(None, 1)
         self.op = parts[0]
-        # operands up to the first modifier-only token (offset:, off, glc, ...)
+        # comma-separated operands; modifiers after the last one (offset:, glc, ...) stay
+        # attached to it and are dropped where registers are read
         self.ops = _split_ops(parts[1]) if len(parts) > 1 else []
         self.asm = asm
         self.text = text
@@ -90,9 +91,9 @@ class Ins:
         return [], []
 
 
-def _functions(text):
-    """{kernel name: [Ins | ('label', name)]} in layout order."""
-    funcs, cur, name, in_asm = {}, None, None, False
+def _body(text):
+    """Instructions and labels of one function's body, in layout order."""
+    items, in_asm = [], False
     for raw in text.splitlines():
         line = raw.strip()
         if line.startswith(";;#ASMSTART"):
@@ -101,41 +102,25 @@ def _functions(text):
         if line.startswith(";;#ASMEND"):
             in_asm = False
             continue
-        if name is None:
-            m = LABEL.match(line)
-            if m and m.group(1).startswith("_Z") and cur is None and pending == m.group(1):
-                name, cur = m.group(1), []
-            continue
-        if line.startswith(".Lfunc_end"):
-            funcs[name] = cur
-            name, cur = None, None
-            continue
         if not line or line.startswith((";", "//")):
             continue
         m = LABEL.match(line)
         if m:
-            cur.append(("label", m.group(1)))
+            items.append(("label", m.group(1)))
             continue
         if line.startswith("."):
             continue
-        cur.append(Ins(line.split(";")[0].split("//")[0].strip(), in_asm))
-    return funcs
-
-
-pending = None
+        items.append(Ins(line.split(";")[0].split("//")[0].strip(), in_asm))
+    return items
 
 
 def _parse(text):
-    """_functions with the kernel symbols found from their .type directives."""
-    global pending
+    """{kernel symbol: body items} for every function the assembly defines."""
     funcs = {}
-    names = set(re.findall(r"\.type\s+(_Z\w+),@function", text))
-    for nm in names:
-        pending = nm
-        i = text.index(f"\n{nm}:")
+    for name in set(re.findall(r"\.type\s+(_Z\w+),@function", text)):
+        i = text.index(f"\n{name}:") + len(name) + 2
         j = text.index(".Lfunc_end", i)
-        funcs.update(_functions(text[i:j] + "\n.Lfunc_end\n"))
-    pending = None
+        funcs[name] = _body(text[i:j])
     return funcs
 
 
@@ -190,10 +175,9 @@ def _run_block(ins, state, errors=None):
             exempt = set()
             if x.is_product and len(x.ops) >= 4 and x.ops[3].split()[0] == x.ops[0].split()[0]:
                 exempt = set(dst)  # accumulation chain: source C is the destination
-            ab = set(src[: len(src)]) if not x.is_product else set(
-                r for o in x.ops[1:3] for r in _regs(o.split()[0]))
-            touched = (set(dst) | set(src)) if not x.is_product else (ab | (set(dst) - exempt) |
-                                                                        (set(src) - ab - exempt))
+            # sources A and B of a product; every other access of a non-product
+            ab = set(r for o in x.ops[1:3] for r in _regs(o.split()[0])) if x.is_product else set()
+            touched = (ab | (set(dst) - exempt) | (set(src) - ab - exempt)) if x.is_product else set(dst) | set(src)
             kinds = ("pa", "pc") if x.asm else ("pa",)
             for k in kinds:
                 for r in touched:
