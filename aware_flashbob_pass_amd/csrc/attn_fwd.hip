@@ -11,6 +11,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// 1: non-causal 16-bit d = 64 sweeps take the skewed kernel; 0 builds them with
+// attn_fwd_kernel instead (for comparing the two on the same inputs).
 #ifndef FB_FWD_SKEW
 #define FB_FWD_SKEW 1
 #endif
