@@ -36,7 +36,8 @@ buffers of score operands (K, V, UK, UV rows), a[208:239] two buffers of transpo
 operands (K^T, UK^T, V^T, UV^T). SGPRs: s[40:47] the copy sources of K, V, UK, UV (row
 block of step j + AHEAD), s48 the wave's LDS base, s49 the steps of the whole sweep (the
 copies run ahead to its end, also past the block's last step), s50 the step index, s51
-the block's step count, s52 scratch, s53 log2(e), s54 the caller's m0.
+the block's step count, s52 scratch, s53 log2(e), s54 the caller's m0, s55 packed bf16
+(1, 1) for the row sums (DOT_SUMS).
 
 Options kept for measurement (all produce the same results): the LDS operands in VGPRs
 (OPERANDS = "v"; no faster), more LDS stages and a longer copy distance (NBUF, AHEAD;
@@ -56,7 +57,8 @@ HIGH_BASE = 184          # with more than 4 slots: v[184:187] row and v[188:191]
                          # addresses of slots 4.. (64 KiB further on: beyond a 16-bit offset)
 LOG2E_BITS = 0x3FB8AA3B
 
-# How the element-wise work (11 vector instructions per element, 8 pairs of elements)
+# How the element-wise work (10 vector instructions per element with DBIAS, 8 pairs of
+# elements)
 # rides along the matrix-core products: pairs PAIRS_A of the step during its 20 score
 # products (VALU_FIRST before the first, VALU_PER_SCORE after each, the rest after the
 # last), pairs PAIRS_B during the 12 accumulating products of k-step 0 (VALU_PER_ACC
@@ -82,6 +84,13 @@ OPERANDS = "a"
 # saves its 16 subtractions.
 DBIAS = True
 DBIAS_TILE = 160
+# True: the row sums alpha and e0 of a pair of elements as one v_dot2_f32_bf16 of the
+# pair's packed bf16 weights (P G and w_b, the values the accumulating products use)
+# against packed (1, 1) in s55, instead of two float32 additions each: 16 fewer vector
+# instructions per step and the same errors against the oracle, but pass 1 ran 2.5%
+# slower (315 vs 307 us at N = 16384). False: the float32 additions.
+DOT_SUMS = False
+ONES_BF16X2 = 0x3F803F80
 
 
 def operand_bases():
@@ -141,7 +150,8 @@ def vrange(base, n):
 
 
 def element_pair(p, cur, tmp, sums=(254, 255), init=False):
-    """The element-wise work of elements 2p and 2p + 1 of the tiles at `cur` (22 VALU):
+    """The element-wise work of elements 2p and 2p + 1 of the tiles at `cur` (20 vector
+    instructions; 18 with DOT_SUMS, 22 without DBIAS):
     p = exp2(S log2(e) - L log2(e)), t = dP - D, alpha += p G, w_b = p (G t + H),
     e0 += w_b, and the bf16 weights W_a = p t, W_b = w_b, P = p, P G.
     tmp: 8 temporaries (P0, P1, T0, T1, PG0, PG1, WB0, WB1); sums: the registers
@@ -166,22 +176,31 @@ def element_pair(p, cur, tmp, sums=(254, 255), init=False):
             out.append((f"v_sub_f32 v{T[i]}, v{DP[i]}, v253", T[i], [DP[i], 253], False))
     for i in range(2):
         out.append((f"v_mul_f32 v{PG[i]}, v{P[i]}, v{G[i]}", PG[i], [P[i], G[i]], False))
-    for i in range(2):
-        src = "0" if init and i == 0 else f"v{al}"
-        out.append((f"v_add_f32 v{al}, {src}, v{PG[i]}", al, [PG[i], al], False))
+    if not DOT_SUMS:
+        for i in range(2):
+            src = "0" if init and i == 0 else f"v{al}"
+            out.append((f"v_add_f32 v{al}, {src}, v{PG[i]}", al, [PG[i], al], False))
     for i in range(2):
         out.append((f"v_fma_f32 v{WB[i]}, v{G[i]}, v{TD[i]}, v{H[i]}", WB[i], [G[i], TD[i], H[i]], False))
     for i in range(2):
         out.append((f"v_mul_f32 v{WB[i]}, v{P[i]}, v{WB[i]}", WB[i], [P[i], WB[i]], False))
-    for i in range(2):
-        src = "0" if init and i == 0 else f"v{e0}"
-        out.append((f"v_add_f32 v{e0}, {src}, v{WB[i]}", e0, [WB[i], e0], False))
+    if not DOT_SUMS:
+        for i in range(2):
+            src = "0" if init and i == 0 else f"v{e0}"
+            out.append((f"v_add_f32 v{e0}, {src}, v{WB[i]}", e0, [WB[i], e0], False))
     for i in range(2):
         out.append((f"v_mul_f32 v{T[i]}, v{P[i]}, v{TD[i]}", T[i], [P[i], TD[i]], False))
     t, reg = (2 * p) >> 3, ((2 * p) & 7) >> 1
+    packed = {}
     for base, src in ((128, T), (136, WB), (144, P), (152, PG)):
         d = base + 4 * t + reg
+        packed[base] = d
         out.append((f"v_cvt_pk_bf16_f32 v{d}, v{src[0]}, v{src[1]}", d, [src[0], src[1]], False))
+    if DOT_SUMS:  # alpha += (P G)_2p + (P G)_2p+1, e0 += w_b,2p + w_b,2p+1 from the packed weights
+        for acc, base in ((al, 152), (e0, 136)):
+            src = "0" if init else f"v{acc}"
+            out.append((f"v_dot2_f32_bf16 v{acc}, v{packed[base]}, s55, {src}", acc,
+                        [packed[base]] + ([] if init else [acc]), False))
     return out
 
 
@@ -363,6 +382,8 @@ def loop_text():
            "s_waitcnt vmcnt(0) lgkmcnt(0)",  # the counts below assume nothing else in flight
            "s_mov_b32 s54, m0",  # m0 is the compiler's: restored at the end
            f"s_mov_b32 s53, 0x{LOG2E_BITS:08x}", "s_mov_b32 s50, 0"]
+    if DOT_SUMS:
+        ins.append(f"s_mov_b32 s55, 0x{ONES_BF16X2:08x}")
     assert sorted(PAIRS_A + PAIRS_B + PAIRS_C) == list(range(8))
     assert not DBIAS or OPERANDS == "a"
     assert 3 <= AHEAD < NBUF and NBUF % 2 == 0 and 4 * (AHEAD - 2) <= 63 and (NBUF <= 4 or OPERANDS == "a")
@@ -422,7 +443,7 @@ def render():
     wv, wa = written_registers(ins)
     assert not set(wv) & set(range(243, 254)) and not set(wa) & set(range(128, 176)), "block writes an input"
     clob = ", ".join([f'"v{r}"' for r in wv if r not in BOUND_V] + [f'"a{r}"' for r in wa if r not in BOUND_A])
-    clob += ', "s50", "s52", "s53", "s54", "scc", "memory"'
+    clob += ', "s50", "s52", "s53", "s54"' + (', "s55"' if DOT_SUMS else "") + ', "scc", "memory"'
     return ("// Generated by gen_pass1_asm.py (same directory); do not edit by hand.\n"
             "// The step loop of pass 1's non-causal d = 64 bf16 sweep with tau folded: the\n"
             "// generator's docstring gives the schedule and the register map.\n"
