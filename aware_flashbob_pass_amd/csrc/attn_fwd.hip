@@ -275,10 +275,30 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_skew_kernel(FwdArgs a) {
   const int nsteps = kt_end - kt_begin;
   auto stage = [&](int slot, int t) __attribute__((always_inline)) { return lds + (slot * NT + t) * G::ROW_ELEMS; };
   auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
+  // Copies of whole 32-key blocks take the scalar-base form: the block's address is
+  // wave-uniform, the lane's byte offset within it (the slot stage_direct gives the lane,
+  // with its swizzle) is computed once, and the LDS destination is the wave's part of the
+  // stage. The ragged last block keeps stage_direct, which repeats row N - 1.
+  static_assert(stage_copies<D, kBlock / 64>() == 1, "one copy per wave and tensor");
+  const int cslot = wave * 64 + lane, crow = cslot / (D / 8);
+  const unsigned coff = 2u * (unsigned)(crow * D + (((cslot % (D / 8)) ^ swz<D>(crow)) << 3));
+  const unsigned lds_wave = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) void*)lds + (unsigned)wave * 1024u);
   auto issue = [&](int slot, int j) __attribute__((always_inline)) {
+    const int r0 = (kt_begin + j) * kTile;
+    if (r0 + kTile <= N) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      stage_direct<TT, D, kBlock / 64, true>(src[t], (kt_begin + j) * kTile, N, stage(slot, t), wave, lane);
+      for (int t = 0; t < NT; ++t) {
+        const T* blk = src[t] + (size_t)r0 * D;
+        const unsigned m0 = lds_wave + (unsigned)((slot * NT + t) * G::ROW_ELEMS * (int)sizeof(T));
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(coff), "s"(blk), "{m0}"(m0)
+                     : "memory");
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        stage_direct<TT, D, kBlock / 64, true>(src[t], r0, N, stage(slot, t), wave, lane);
+    }
   };
 
   V bq[DK];
@@ -311,7 +331,9 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_skew_kernel(FwdArgs a) {
     }
     const int k0 = (kt_begin + j) * kTile;
     const bool masked = k0 + kTile > N || (CAUSAL && k0 + kTile - 1 > q0);  // wave-uniform
-    if (masked || __ballot(lazy_redo(ls, lazy_limit<TT>()))) {
+    // the ballot first, so that the sum and its test stay with the products and exponentials
+    const bool redo = __ballot(lazy_redo(ls, lazy_limit<TT>())) != 0;
+    if (redo || masked) {
       bool keep[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
