@@ -279,21 +279,18 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_skew_kernel(FwdArgs a) {
   // wave-uniform, the lane's byte offset within it (the slot stage_direct gives the lane,
   // with its swizzle) is computed once, and the LDS destination is the wave's part of the
   // stage. The ragged last block keeps stage_direct, which repeats row N - 1.
-  static_assert(stage_copies<D, kBlock / 64>() == 1, "one copy per wave and tensor");
-  const int cslot = wave * 64 + lane, crow = cslot / (D / 8);
-  const unsigned coff = 2u * (unsigned)(crow * D + (((cslot % (D / 8)) ^ swz<D>(crow)) << 3));
-  const unsigned lds_wave = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) void*)lds + (unsigned)wave * 1024u);
+  constexpr int CP = stage_copies<D, kBlock / 64>();
+  unsigned coff[CP];
+#pragma unroll
+  for (int p = 0; p < CP; ++p) coff[p] = stage_lane_offset<D, kBlock / 64>(p, wave, lane);
+  const unsigned lds_wave = lds_addr(lds) + (unsigned)wave * 1024u;
   auto issue = [&](int slot, int j) __attribute__((always_inline)) {
     const int r0 = (kt_begin + j) * kTile;
     if (r0 + kTile <= N) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const T* blk = src[t] + (size_t)r0 * D;
-        const unsigned m0 = lds_wave + (unsigned)((slot * NT + t) * G::ROW_ELEMS * (int)sizeof(T));
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(coff), "s"(blk), "{m0}"(m0)
-                     : "memory");
-      }
+      for (int t = 0; t < NT; ++t)
+        stage_block_saddr<D, kBlock / 64>(src[t] + (size_t)r0 * D, coff,
+                                          lds_wave + (unsigned)((slot * NT + t) * G::ROW_ELEMS * (int)sizeof(T)));
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t)

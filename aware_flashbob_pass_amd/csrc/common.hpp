@@ -279,6 +279,38 @@ __device__ inline void stage_direct(const typename TT::elem* __restrict__ src, i
   }
 }
 
+// The same copies for a whole 32-row block (every row below N) in the scalar-base form:
+// the block's address is wave-uniform and each lane's byte offset within it, which is the
+// same for every block, is computed once (stage_lane_offset), so a step spends no vector
+// instructions on addresses. lds_tile_wave: the LDS byte address of the tile plus
+// 1024 wave (wave-uniform). The s_nop covers the M0 write -> LDS-DMA hazard.
+template <int D, int NWAVES, int L = 0>
+__device__ inline unsigned stage_lane_offset(int p, int wave, int lane) {
+  constexpr int SPR = D / 8;
+  const int slot = (p * NWAVES + wave) * 64 + lane, row = slot / SPR;
+  return 2u * (unsigned)(row * D + (((slot % SPR) ^ swz<D, L>(row)) << 3));
+}
+template <int D, int NWAVES>
+__device__ inline void stage_block_saddr(const void* block, const unsigned (&off)[stage_copies<D, NWAVES>()],
+                                         unsigned lds_tile_wave) {
+#pragma unroll
+  for (int p = 0; p < stage_copies<D, NWAVES>(); ++p) {
+    const unsigned m0 = lds_tile_wave + (unsigned)(p * NWAVES * 1024);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(off[p]), "s"(block), "{m0}"(m0)
+                 : "memory");
+  }
+}
+// 4 bytes per lane in the scalar-base form: lane l's value (at byte off of src) lands at
+// LDS byte address lds + 4 l.
+__device__ inline void glds4_saddr(const void* src, unsigned off, unsigned lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1 offset:0" ::"v"(off), "s"(src), "{m0}"(lds) : "memory");
+}
+// The LDS byte address of an LDS pointer, wave-uniform.
+template <class P>
+__device__ inline unsigned lds_addr(const P* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const void*)p);
+}
+
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Unrolled runs of pipeline steps with compile-time stage indices: unroll_steps
 // calls f(integral_constant<int, I>, j0 + I) for every I of the sequence;

@@ -192,13 +192,31 @@ __global__ __launch_bounds__(kBlock, (D == 64 ? 2 : 1)) void bob_pass2_kernel(Pa
   // + H); the first backward stages L and D and scales L here. Wave w copies
   // scalar w % NSCAL with its lanes 0..31, so every wave issues the same number of
   // copies per stage (with NSCAL = 2 two waves write the same values).
+  // Whole 32-row blocks take the scalar-base copies (no per-step address arithmetic);
+  // the ragged last block keeps stage_direct and glds4, which repeat row N - 1.
+  constexpr int CP = stage_copies<D, kBlock / 64>();
+  unsigned coff[CP];
+#pragma unroll
+  for (int p = 0; p < CP; ++p) coff[p] = stage_lane_offset<D, kBlock / 64>(p, wave, lane);
+  const unsigned lds_wave = lds_addr(lds) + (unsigned)wave * 1024u;
   auto issue = [&](int stg, int j) {
     const int i0 = (it_begin + j) * kTile;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (!FIRST || t < 2) stage_direct<TT, D, kBlock / 64, true>(src[t], i0, N, tile(stg, t), wave, lane);
     const int which = wave % NSCAL;
-    if (lane < kTile) glds4<true>(vsrc[which] + min(i0 + lane, N - 1), scal(stg) + which * kTile);
+    if (i0 + kTile <= N) {
+      const unsigned stage_bytes = (unsigned)((stg % NBUF) * STAGE_ELEMS * (int)sizeof(T));
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (!FIRST || t < 2)
+          stage_block_saddr<D, kBlock / 64>(src[t] + (size_t)i0 * D, coff,
+                                            lds_wave + stage_bytes + (unsigned)(t * G::ROW_ELEMS * (int)sizeof(T)));
+      if (lane < kTile)
+        glds4_saddr(vsrc[which] + i0, (unsigned)lane * 4u, lds_addr(scal(stg) + which * kTile));
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (!FIRST || t < 2) stage_direct<TT, D, kBlock / 64, true>(src[t], i0, N, tile(stg, t), wave, lane);
+      if (lane < kTile) glds4<true>(vsrc[which] + min(i0 + lane, N - 1), scal(stg) + which * kTile);
+    }
   };
   settle_regs(bk, bv);
   if constexpr (!FIRST) settle_regs(buk, buv);
