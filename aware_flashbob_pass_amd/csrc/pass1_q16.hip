@@ -179,12 +179,30 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_q16_kernel(Pass1Args a) {
   const int kt_end = (int)((long long)(split + 1) * nkt / a.nsplit);
   const int nsteps = kt_end - kt_begin;
   auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * 32 <= q0 + kQRows - 1; };
-  auto issue = [&](int stg, int j) {
+  // Copies from inline assembly (the compiler's own waits then never drain them early):
+  // whole 32-key blocks in the scalar-base form, the ragged last block through
+  // stage_direct, which repeats row N - 1. Each step ends with every copy landed.
+  constexpr int CP = stage_copies<kQD, kQWaves>();
+  unsigned coff[CP];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      stage_direct<TT, kQD, kQWaves, false, kQLayout>(src[t], (kt_begin + j) * 32, N, lds + stg * kQStageElems + t * kQTileElems,
-                                      wave, lane);
+  for (int p = 0; p < CP; ++p) coff[p] = stage_lane_offset<kQD, kQWaves, kQLayout>(p, wave, lane);
+  const unsigned lds_wave = lds_addr(lds) + (unsigned)wave * 1024u;
+  auto issue = [&](int stg, int j) {
+    const int r0 = (kt_begin + j) * 32;
+    if (r0 + 32 <= N) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        stage_block_saddr<kQD, kQWaves>(src[t] + (size_t)r0 * kQD, coff,
+                                        lds_wave + (unsigned)((stg * kQStageElems + t * kQTileElems) * (int)sizeof(T)));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        stage_direct<TT, kQD, kQWaves, true, kQLayout>(src[t], r0, N, lds + stg * kQStageElems + t * kQTileElems,
+                                                      wave, lane);
+    }
   };
+  settle_regs(bq, bdo, buq);
+  settle_regs(lq, dq);
   for (int j = 0; j < kQNBuf - 1 && j < nsteps; ++j) issue(j, j);
   wait_vmem();
   __syncthreads();
