@@ -149,12 +149,28 @@ __global__ __launch_bounds__(kBlock, 2) void attn_fwd_kernel(FwdArgs a) {
   auto stage = [&](int j, int t) { return lds + ((j % NBUF) * NT + t) * G::ROW_ELEMS; };
   auto active = [&](int j) { return !CAUSAL || (kt_begin + j) * kTile <= q0 + kTile - 1; };
 
-  auto issue = [&](int stg, int j) {
+  // Copies from inline assembly: whole 32-key blocks in the scalar-base form, the ragged
+  // last block through stage_direct (which repeats row N - 1); each step ends with every
+  // copy landed.
+  constexpr int CP = stage_copies<D, kBlock / 64>();
+  unsigned coff[CP];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      stage_direct<TT, D, kBlock / 64>(src[t], (kt_begin + j) * kTile, N, lds + (stg * NT + t) * G::ROW_ELEMS, wave,
-                                        lane);
+  for (int p = 0; p < CP; ++p) coff[p] = stage_lane_offset<D, kBlock / 64>(p, wave, lane);
+  const unsigned lds_wave = lds_addr(lds) + (unsigned)wave * 1024u;
+  auto issue = [&](int stg, int j) {
+    const int r0 = (kt_begin + j) * kTile;
+    if (r0 + kTile <= N) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        stage_block_saddr<D, kBlock / 64>(src[t] + (size_t)r0 * D, coff,
+                                          lds_wave + (unsigned)((stg * NT + t) * G::ROW_ELEMS * (int)sizeof(T)));
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        stage_direct<TT, D, kBlock / 64, true>(src[t], r0, N, lds + (stg * NT + t) * G::ROW_ELEMS, wave, lane);
+    }
   };
+  settle_regs(bq);
   for (int j = 0; j < 2 && j < nsteps; ++j) issue(j, j);
   wait_vmem();
   __syncthreads();
