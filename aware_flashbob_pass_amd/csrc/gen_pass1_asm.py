@@ -91,6 +91,12 @@ DBIAS_TILE = 160
 # slower (315 vs 307 us at N = 16384). False: the float32 additions.
 DOT_SUMS = False
 ONES_BF16X2 = 0x3F803F80
+# Steps per workgroup barrier in the loop's full groups: 1, or 2 (a barrier after every
+# second step; it then has to publish the stages of the next two steps, so copies run at
+# least four steps ahead, and a copy issued while a slower wave is still one step behind
+# must not overwrite what that wave reads: NBUF >= AHEAD + 2). Tail steps keep one
+# barrier each, so the block always ends with its stages published.
+BARRIER_EVERY = 1
 
 
 def operand_bases():
@@ -346,8 +352,9 @@ def step_body(S):
     return st.ins
 
 
-def step_text(S, label):
-    """One complete step: guarded copies, the body, the copy wait and the barrier."""
+def step_text(S, label, tail=False):
+    """One complete step: guarded copies, the body, the copy wait and the barrier (with
+    BARRIER_EVERY = 2, only after odd steps of a full group)."""
     ins = []
     ins.append("s_add_u32 s52, s50, %d" % AHEAD)
     ins.append("s_cmp_lt_u32 s52, s49")
@@ -362,17 +369,21 @@ def step_text(S, label):
     for k in range(4):  # the copy sources advance by one 32-row block every step
         ins.append(f"s_add_u32 s{40 + 2 * k}, s{40 + 2 * k}, {TILE_BYTES}")
         ins.append(f"s_addc_u32 s{41 + 2 * k}, s{41 + 2 * k}, 0")
-    ins.append("s_add_u32 s52, s50, %d" % AHEAD)
-    ins.append("s_cmp_lt_u32 s52, s49")
-    ins.append(f"s_cbranch_scc0 L_wait0_{label}_%=")
-    # the copies of step j + 2 (read from step j + 1 on) have landed; those of the
-    # AHEAD - 2 latest steps may stay in flight
-    ins.append(f"s_waitcnt vmcnt({4 * (AHEAD - 2)})")
-    ins.append(f"s_branch L_waited_{label}_%=")
-    ins.append(f"L_wait0_{label}_%=:")
-    ins.append("s_waitcnt vmcnt(0)")
-    ins.append(f"L_waited_{label}_%=:")
-    ins.append("s_barrier")
+    per_step = BARRIER_EVERY == 1 or tail
+    if per_step or S % 2 == 1:
+        # per step: the copies of step j + 2 (read from step j + 1 on) have landed, those of
+        # the AHEAD - 2 latest steps may stay in flight; every second step: those of steps
+        # j + 2 and j + 3 (read by the next two steps), AHEAD - 3 in flight
+        keep = AHEAD - 2 if per_step else AHEAD - 3
+        ins.append("s_add_u32 s52, s50, %d" % AHEAD)
+        ins.append("s_cmp_lt_u32 s52, s49")
+        ins.append(f"s_cbranch_scc0 L_wait0_{label}_%=")
+        ins.append(f"s_waitcnt vmcnt({4 * keep})")
+        ins.append(f"s_branch L_waited_{label}_%=")
+        ins.append(f"L_wait0_{label}_%=:")
+        ins.append("s_waitcnt vmcnt(0)")
+        ins.append(f"L_waited_{label}_%=:")
+        ins.append("s_barrier")
     ins.append("s_add_u32 s50, s50, 1")
     return ins
 
@@ -387,6 +398,7 @@ def loop_text():
     assert sorted(PAIRS_A + PAIRS_B + PAIRS_C) == list(range(8))
     assert not DBIAS or OPERANDS == "a"
     assert 3 <= AHEAD < NBUF and NBUF % 2 == 0 and 4 * (AHEAD - 2) <= 63 and (NBUF <= 4 or OPERANDS == "a")
+    assert BARRIER_EVERY in (1, 2) and (BARRIER_EVERY == 1 or (AHEAD >= 4 and NBUF >= AHEAD + 2))
     if NBUF > 4:  # addresses of the upper slots
         ins += [f"v_add_u32 v{HIGH_BASE + i}, 0x10000, v{244 + i}" for i in range(8)]
     if DBIAS:  # the -D tile, and step 0's dP tile (formed by the caller) less D
@@ -410,7 +422,7 @@ def loop_text():
     for S in range(NBUF - 1):
         ins.append("s_cmp_ge_u32 s50, s51")
         ins.append("s_cbranch_scc1 L_end_%=")
-        ins += step_text(S, f"t{S}")
+        ins += step_text(S, f"t{S}", tail=True)
     ins.append("L_end_%=:")
     ins += ["s_mov_b32 m0, s54", "s_nop 7", "s_nop 7", "s_nop 7"]  # the last accumulating products complete
     return ins

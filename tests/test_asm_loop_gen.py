@@ -159,7 +159,8 @@ def test_generated_loop_uses_only_listed_scalar_instructions():
 
 @pytest.mark.parametrize("over", [dict(OPERANDS="v", DBIAS=False, PAIRS_A=(0, 1, 2, 3), PAIRS_B=(4, 5, 6, 7),
                                        PAIRS_C=(), VALU_FIRST=12, VALU_PER_SCORE=4, VALU_PER_ACC=8),
-                                  dict(NBUF=8, AHEAD=6), dict(DOT_SUMS=False)])
+                                  dict(NBUF=8, AHEAD=6), dict(DOT_SUMS=True),
+                                  dict(NBUF=6, AHEAD=4, BARRIER_EVERY=2)])
 def test_generator_options_replay(over):
     """The options kept for measurement generate schedules that pass the same replay."""
     g = _gen()
