@@ -42,7 +42,8 @@ COMMON_FLAGS = [
 # take the matrix-core VGPR form for their score products (their accumulators are
 # AGPR inline assembly); the flag applies to their whole files, which hold nothing else.
 EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "bob_pass2_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "bob_pass2_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "pass1_q16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -403,6 +403,23 @@ __device__ inline void acc_settle(f32x16 (&A)[MB], f32x16 (&B)[MB]) {
   for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(A[mb]), "+a"(B[mb]));
 }
 
+// The same for 16 x 16 x 32 products on 16 x 16 float32 tiles (four values a lane), and
+// the settle of four arrays of such tiles (an 8-pass product's result needs 10 wait states;
+// 24 are given).
+template <class TT>
+__device__ inline void mfma16_acc(f32x4& acc, typename TT::vec a, typename TT::vec b) {
+  if constexpr (std::is_same_v<TT, BF16>)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int M>
+__device__ inline void acc16_settle(f32x4 (&A)[M], f32x4 (&B)[M], f32x4 (&C)[M], f32x4 (&X)[M]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int m = 0; m < M; ++m) asm volatile("" : "+a"(A[m]), "+a"(B[m]), "+a"(C[m]), "+a"(X[m]));
+}
+
 // Index of the calling wave in its workgroup as a wave-uniform (scalar)
 // value, so that branches and offsets derived from it stay scalar.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }

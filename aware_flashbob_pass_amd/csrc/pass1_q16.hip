@@ -13,6 +13,9 @@
 // registers, each score tile is computed once, and a workgroup of 4 waves (one per
 // SIMD) holds 64 queries.
 //
+// The file is compiled in the matrix-core VGPR form (score tiles in VGPRs, no copies
+// out of AGPRs); the four accumulators stay in AGPRs through inline-assembly products
+// (mfma16_acc), which supply their own hazard waits and settle after the sweep.
 // Products are v_mfma_f32_16x16x32 (16-bit operands, float32 accumulation; lane
 // layout checked on the MI355X with an in-bounds probe: A lane l holds row l % 16
 // and k = 8 (l / 16) .. + 7, B lane l column l % 16 and the same k, D lane l
@@ -273,12 +276,12 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_q16_kernel(Pass1Args a) {
         const V ouk = q16_tr_op<TT>(tuk, mt, lane);
         const V ov = q16_tr_op<TT>(tv, mt, lane);
         const V ouv = q16_tr_op<TT>(tuv, mt, lane);
-        accA[mt] = mfma_16x16x32<TT>(ouk, wa, accA[mt]);  // W_a UK
-        accB[mt] = mfma_16x16x32<TT>(ok, wa, accB[mt]);   // W_a K
-        accX[mt] = mfma_16x16x32<TT>(ouv, pp, accX[mt]);  // P UV
-        accA[mt] = mfma_16x16x32<TT>(ok, wb, accA[mt]);   // W_b K
-        accC[mt] = mfma_16x16x32<TT>(ok, pp, accC[mt]);   // P K
-        accX[mt] = mfma_16x16x32<TT>(ov, pg, accX[mt]);   // (P G) V
+        mfma16_acc<TT>(accA[mt], ouk, wa);  // W_a UK
+        mfma16_acc<TT>(accB[mt], ok, wa);   // W_a K
+        mfma16_acc<TT>(accX[mt], ouv, pp);  // P UV
+        mfma16_acc<TT>(accA[mt], ok, wb);   // W_b K
+        mfma16_acc<TT>(accC[mt], ok, pp);   // P K
+        mfma16_acc<TT>(accX[mt], ov, pg);   // (P G) V
       }
     }
     wait_vmem();
@@ -295,6 +298,7 @@ __global__ __launch_bounds__(kBlock, 1) void bob_pass1_q16_kernel(Pass1Args a) {
   }
   if (j < nsteps) step(I0{}, j);
   if (j + 1 < nsteps) step(I1{}, j + 1);
+  acc16_settle<8>(accA, accB, accC, accX);
 
   if (a.nsplit == 1) {
     // the four lane groups of a query: (x0 + x1) + (x2 + x3) on every lane

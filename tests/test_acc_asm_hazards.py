@@ -35,7 +35,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-FILES = ["bob_pass1_vgpr.hip", "bob_pass2_vgpr.hip"]
+FILES = ["bob_pass1_vgpr.hip", "bob_pass2_vgpr.hip", "pass1_q16.hip"]
 PRODUCT_TO_ACCESS = 19
 VALU_TO_PRODUCT = 2
 CAP = 32  # gaps at or above this no longer matter
