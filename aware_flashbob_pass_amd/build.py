@@ -38,9 +38,11 @@ COMMON_FLAGS = [
 # non-finite value in that file (the lazy rescale trigger) compares bit patterns
 # as integers, which that flag does not touch; api.cpp checks its arguments with
 # NaN semantics intact. Inputs are assumed finite.
-# The two-pass sweeps of pass 1 (16-bit) and the non-causal d = 128 sweep of pass 2
-# take the matrix-core VGPR form for their score products (their accumulators are
-# AGPR inline assembly); the flag applies to their whole files, which hold nothing else.
+# The two-pass sweeps of pass 1 (16-bit: d = 64 in bob_pass1_vgpr.hip, the 16-query
+# d = 128 kernel in pass1_q16.hip) and the non-causal d = 128 sweep of pass 2 take the
+# matrix-core VGPR form for their score products (their accumulators are AGPR inline
+# assembly); the flag applies to their whole files, which hold nothing else with
+# matrix-core products (pass1_q16.hip's merge kernel has none).
 EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "bob_pass1_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "bob_pass2_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "pass1_q16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
